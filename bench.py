@@ -1,0 +1,252 @@
+"""Benchmark of the per-rank ring-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--sweep] [--verify]
+
+A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
+rank, staging included) over one batch of synthetic input already resident in HBM.
+W untimed warm-up calls, then K calls enqueued back to back on one stream with one
+synchronisation at the end (the measurement protocol of the mKernel paper, §5.1),
+timed with HIP events recorded on that stream. Prints ONE JSON line on stdout.
+
+The default workload is the per-rank share of a 64K-token causal GQA sequence over
+16 ranks (rank 15: the slowest rank of a contiguous causal ring). Throughput counts
+algorithmic FLOPs only: 4 * D * Hq * (visible query-key pairs).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and % bf16 MFMA peak, per-rank ring-attn fwd, 1 MI355X"
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
+PEAK_BF16_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["overlap_attention_amd/csrc/mkra_kernel.hip", "overlap_attention_amd/csrc/mkra_args.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(cfg):
+    if cfg.causal:
+        pairs = cfg.rank * cfg.lq * cfg.lk + cfg.lq * (cfg.lq + 1) // 2
+    else:
+        pairs = cfg.n_chunks * cfg.lq * cfg.lk
+    return 4 * cfg.d * cfg.hq * pairs
+
+
+def algorithmic_bytes(cfg):
+    """Q + the KV chunks read once + staged copies (read + write of the non-local
+    chunks the ring moves) + out + lse."""
+    q = cfg.lq * cfg.hq * cfg.d * 2
+    chunk = 2 * cfg.lk * cfg.hkv * cfg.d * 2
+    steps = cfg.n_steps
+    return q + steps * chunk + 2 * (steps - 1) * chunk + q + cfg.hq * cfg.lq * 4
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sha") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, kv, budget_rows):
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload:
+    `budget_rows` query rows spread over the chunk, all heads, all keys."""
+    import numpy as np
+
+    import oracle
+    from ring_inputs import to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rows = np.linspace(0, cfg.lq - 1, budget_rows).astype(np.int64)
+    q64, kv64 = to_f64(q), to_f64(kv)
+    t0 = time.perf_counter()
+    oracle.ring_attention_rows(q64, kv64, cfg.rank, cfg.causal, cfg.gqa_ratio, rows)
+    dt = time.perf_counter() - t0
+    if cfg.causal:
+        pairs = sum(cfg.rank * cfg.lk + int(r) + 1 for r in rows)
+    else:
+        pairs = len(rows) * cfg.n_chunks * cfg.lk
+    flops = 4 * cfg.d * cfg.hq * pairs
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {cfg.lq} query rows (evenly spaced), all {cfg.hq} heads, all visible keys; "
+                  f"{dt:.1f} s on {threads} threads of {cpu or 'the host CPU'}; fp64 NumPy/BLAS, dense over "
+                  f"masked keys too (FLOPs counted for visible pairs only)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="name of a workload in ring_inputs.CONFIGS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--sweep", action="store_true", help="also time fixed staging splits vs adaptive (stderr)")
+    ap.add_argument("--verify", action="store_true", help="check sampled rows against the oracle (stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import overlap_attention_amd as mk
+    from ring_inputs import CONFIGS, CONFIG_BY_NAME, make_inputs
+
+    cfg = CONFIG_BY_NAME[args.workload] if args.workload else CONFIGS[2]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {cfg.name}: generating inputs")
+    q, kv = make_inputs(cfg, seed=CONFIGS.index(cfg) if cfg in CONFIGS else 0)
+    qg, kvg = q.cuda(), kv.cuda()
+    out = torch.empty_like(qg)
+    lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(opts=None):
+        if opts is None:
+            mk.mk_ring_attn_fwd(qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, out, lse, stream=stream)
+        else:
+            mk.mk_ring_attn_fwd_ex(qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, out, lse,
+                                   stream=stream, opts=opts)
+
+    def timed(k, opts=None):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(k):
+            step(opts)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / k  # ms per launch
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mk.mk_ring_attn_status()
+    log(f"[bench] timing {args.steps} launches")
+    t_host0 = time.perf_counter()
+    ms = timed(args.steps)
+    t_host = time.perf_counter() - t_host0
+    mk.mk_ring_attn_status()
+    flops = algorithmic_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/launch, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
+        f"host wall {t_host:.3f} s")
+
+    stats = mk.ring_attn_fwd(qg, kvg, cfg.rank, cfg.causal, cfg.gqa_ratio, want_stats=True)[2]
+    log(f"[bench] stats {stats}")
+
+    if args.verify:
+        import oracle
+        from ring_inputs import to_f64
+        from tests.parity import compare, fmt, sample_rows
+
+        rows = sample_rows(cfg.lq, n_random=8, seed=1)
+        ro, rl = oracle.ring_attention_rows(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio, rows)
+        rep = compare(to_f64(out[rows]), lse[:, rows].double().cpu().numpy(), ro, rl)
+        log(f"[bench] verify: {fmt(rep)}")
+
+    if args.sweep:
+        res = {}
+        for n in (1, 2, 4, 8, 16, 32, 64):
+            res[f"fixed{n}"] = timed(max(3, args.steps // 3), mk.default_opts(split_mode=mk.MK_SPLIT_FIXED,
+                                                                             fixed_staging_wgs=n))
+        res["adaptive"] = timed(max(3, args.steps // 3))
+        best = min(v for k, v in res.items() if k != "adaptive")
+        log("[bench] sweep (ms/launch, latency / best fixed): " +
+            ", ".join(f"{k}={v:.3f} ({v / best:.2f}x)" for k, v in res.items()))
+
+    traffic = stored_traffic(cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "rank": cfg.rank,
+            "n_chunks": cfg.n_chunks,
+            "lq": cfg.lq,
+            "lk": cfg.lk,
+            "hq": cfg.hq,
+            "hkv": cfg.hkv,
+            "head_dim": cfg.d,
+            "causal": cfg.causal,
+            "algorithmic_flops": flops,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(cfg),
+            "kernel": "mkra::ring_attn_kernel<%d>" % cfg.d,
+        },
+        "staging": {
+            "initial_target": stats["initial_target"],
+            "final_target": stats["final_target"],
+            "max_staging_wgs": stats["max_staging_wgs"],
+            "grid_wgs": stats["grid_wgs"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        line["cpu_baseline"] = cpu_baseline(cfg, q, kv, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

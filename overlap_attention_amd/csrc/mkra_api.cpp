@@ -1,0 +1,466 @@
+// C-ABI layer of mkra: argument validation (on the host, before anything is
+// enqueued), the per-(device, stream) workspace, the decomposition of the problem
+// into compute units and staging tasks, the initial staging split, and the launch of
+// the persistent kernel. See include/mkra.h for the contract of each entry point.
+#include "../../include/mkra.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "mkra_args.h"
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_kernel_launch(const mkra::KernelArgs* a,
+                                                                              hipStream_t stream);
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_kernel_occupancy(int d, int* blocks_per_cu);
+
+namespace {
+
+using mkra::DevCtrl;
+using mkra::DevStatus;
+using mkra::TraceRec;
+
+thread_local std::string g_last_error;
+
+mk_status fail(mk_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+mk_status hip_fail(hipError_t e, const char* what) {
+  return fail(MK_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct Workspace {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  uint64_t epoch = 0;
+  DevCtrl* ctrl = nullptr;
+  DevStatus* status = nullptr;
+  uint32_t* done_count = nullptr;
+  size_t done_cap = 0;
+  uint64_t* slot_flags = nullptr;
+  size_t tiles_cap = 0;
+  uint32_t* tile_parts = nullptr;
+  size_t parts_cap = 0;
+  uint64_t* unit_flags = nullptr;
+  size_t units_cap = 0;
+  uint16_t* slots = nullptr;
+  size_t slot_elems_cap = 0;
+  float* acc = nullptr;
+  size_t acc_cap = 0;
+  TraceRec* trace = nullptr;
+  int trace_cap = 0;
+  bool traced_last = false;
+};
+
+std::mutex g_mu;
+std::vector<Workspace*> g_ws;
+
+struct DeviceInfo {
+  int cus = 0;
+  int occ[2] = {0, 0};  // blocks per CU for D = 64, 128
+};
+std::vector<DeviceInfo> g_dev;
+
+template <class T>
+hipError_t grow(T** p, size_t* cap, size_t need, hipStream_t s, bool zero) {
+  if (need <= *cap && *p != nullptr) return hipSuccess;
+  hipError_t e;
+  if (*p != nullptr) {
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    if ((e = hipFree(*p)) != hipSuccess) return e;
+    *p = nullptr;
+    *cap = 0;
+  }
+  size_t n = std::max<size_t>(need, 1);
+  if ((e = hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T))) != hipSuccess) return e;
+  if (zero && (e = hipMemsetAsync(*p, 0, n * sizeof(T), s)) != hipSuccess) return e;
+  *cap = n;
+  return hipSuccess;
+}
+
+void free_ws(Workspace* w) {
+  if (w->stream != nullptr || w->device >= 0) {
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(w->device);
+    hipStreamSynchronize(w->stream);
+    hipFree(w->ctrl);
+    hipFree(w->status);
+    hipFree(w->done_count);
+    hipFree(w->slot_flags);
+    hipFree(w->tile_parts);
+    hipFree(w->unit_flags);
+    hipFree(w->slots);
+    hipFree(w->acc);
+    hipFree(w->trace);
+    hipSetDevice(cur);
+  }
+  delete w;
+}
+
+Workspace* find_ws(int device, hipStream_t stream, bool create) {
+  for (Workspace* w : g_ws)
+    if (w->device == device && w->stream == stream) return w;
+  if (!create) return nullptr;
+  Workspace* w = new Workspace();
+  w->device = device;
+  w->stream = stream;
+  g_ws.push_back(w);
+  return w;
+}
+
+int64_t numel(const mk_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Contiguous row-major check; strides of extent-1 dimensions are not checked.
+bool contiguous(const mk_tensor* t) {
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+    expect *= t->shape[i];
+  }
+  return true;
+}
+
+mk_status check_tensor(const mk_tensor* t, const char* name, int ndim, int dtype) {
+  if (t == nullptr) return fail(MK_E_INVAL, std::string(name) + ": null descriptor");
+  if (t->ndim != ndim) return fail(MK_E_INVAL, std::string(name) + ": wrong number of dimensions");
+  if (t->dtype != dtype) return fail(MK_E_INVAL, std::string(name) + ": wrong dtype");
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(MK_E_INVAL, std::string(name) + ": negative extent");
+  if (!contiguous(t)) return fail(MK_E_INVAL, std::string(name) + ": not contiguous");
+  if (numel(t) > 0) {
+    if (t->data == nullptr) return fail(MK_E_INVAL, std::string(name) + ": null data pointer");
+    if ((reinterpret_cast<uintptr_t>(t->data) & 15u) != 0)
+      return fail(MK_E_INVAL, std::string(name) + ": data not 16-byte aligned");
+  }
+  return MK_OK;
+}
+
+bool overlaps(const mk_tensor* a, int64_t ea, const mk_tensor* b, int64_t eb) {
+  if (numel(a) == 0 || numel(b) == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a->data), a1 = a0 + numel(a) * ea;
+  uintptr_t b0 = reinterpret_cast<uintptr_t>(b->data), b1 = b0 + numel(b) * eb;
+  return a0 < b1 && b0 < a1;
+}
+
+// Same integer Eq. (2) as the kernel's controller.
+int eq2_target_host(int64_t b, int64_t rp, int64_t rs, int64_t cp, int64_t cs) {
+  if (rs <= 0) return 0;
+  uint64_t ws = (uint64_t)rs * (uint64_t)cs;
+  uint64_t w = ws + (uint64_t)(rp > 0 ? rp : 0) * (uint64_t)cp;
+  int64_t n = (int64_t)((2ull * (uint64_t)b * ws + w) / (2ull * w));
+  int64_t hi = std::min<int64_t>(b - 1, rs);
+  int64_t lo = hi < 1 ? hi : 1;
+  return (int)std::max(lo, std::min(hi, n));
+}
+
+// Largest divisor of g that divides the wave count: query heads per unit.
+int heads_per_unit(int g) {
+  int best = 1;
+  for (int d = 1; d <= mkra::kWaves; ++d)
+    if (g % d == 0 && mkra::kWaves % d == 0) best = d;
+  return best;
+}
+
+mk_status device_info(int dev, DeviceInfo** out) {
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  DeviceInfo& di = g_dev[dev];
+  if (di.cus == 0) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    int o64 = 0, o128 = 0;
+    if ((e = mkra_kernel_occupancy(64, &o64)) != hipSuccess) return hip_fail(e, "occupancy query");
+    if ((e = mkra_kernel_occupancy(128, &o128)) != hipSuccess) return hip_fail(e, "occupancy query");
+    di.cus = prop.multiProcessorCount;
+    di.occ[0] = std::max(o64, 1);
+    di.occ[1] = std::max(o128, 1);
+  }
+  *out = &di;
+  return MK_OK;
+}
+
+mk_status check_device_pointer(const void* p, int dev, const char* name) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MK_E_INVAL, std::string(name) + ": not a HIP allocation");
+  }
+  if (attr.type != hipMemoryTypeDevice || attr.device != dev)
+    return fail(MK_E_INVAL, std::string(name) + ": not device memory of the current device");
+  return MK_OK;
+}
+
+mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, int causal, int gqa, mk_tensor* out,
+              mk_tensor* lse, hipStream_t stream, const mk_ring_attn_opts* user_opts, mk_ring_attn_stats* stats) {
+  g_last_error.clear();
+  mk_ring_attn_opts opts;
+  mk_ring_attn_default_opts(&opts);
+  if (user_opts != nullptr) opts = *user_opts;
+  mk_status s;
+  if ((s = check_tensor(q, "q", 3, MK_BF16)) != MK_OK) return s;
+  if ((s = check_tensor(kv, "kv_chunks", 5, MK_BF16)) != MK_OK) return s;
+  if ((s = check_tensor(out, "out", 3, MK_BF16)) != MK_OK) return s;
+  if ((s = check_tensor(lse, "lse", 2, MK_F32)) != MK_OK) return s;
+  const int64_t lq = q->shape[0], hq = q->shape[1], d = q->shape[2];
+  const int64_t nch = kv->shape[0], lk = kv->shape[2], hkv = kv->shape[3];
+  if (n_chunks < 1 || nch != n_chunks) return fail(MK_E_INVAL, "kv_chunks.shape[0] must equal n_chunks >= 1");
+  if (kv->shape[1] != 2) return fail(MK_E_INVAL, "kv_chunks.shape[1] must be 2 (K, V)");
+  if (rank < 0 || rank >= n_chunks) return fail(MK_E_INVAL, "rank must be in [0, n_chunks)");
+  if (gqa < 1) return fail(MK_E_INVAL, "gqa_ratio must be >= 1");
+  if (kv->shape[4] != d) return fail(MK_E_INVAL, "head_dim of q and kv_chunks differ");
+  if (hq != (int64_t)gqa * hkv) return fail(MK_E_INVAL, "Hq must equal gqa_ratio * Hkv");
+  if (out->shape[0] != lq || out->shape[1] != hq || out->shape[2] != d)
+    return fail(MK_E_INVAL, "out must have the shape of q");
+  if (lse->shape[0] != hq || lse->shape[1] != lq) return fail(MK_E_INVAL, "lse must be [Hq, Lq]");
+  if (causal != 0 && lq != lk) return fail(MK_E_INVAL, "causal needs Lq == Lk");
+  if (overlaps(out, 2, q, 2) || overlaps(out, 2, kv, 2) || overlaps(lse, 4, q, 2) || overlaps(lse, 4, kv, 2) ||
+      overlaps(lse, 4, out, 2))
+    return fail(MK_E_INVAL, "out/lse overlap an input or each other");
+  if (opts.split_mode != MK_SPLIT_ADAPTIVE && opts.split_mode != MK_SPLIT_FIXED)
+    return fail(MK_E_INVAL, "opts.split_mode");
+  if (opts.fixed_staging_wgs < 0 || opts.initial_staging_wgs < 0 || opts.grid_wgs < 0 || opts.spin_timeout_us < 0 ||
+      opts.controller_period_us < 0 || opts.trace_capacity < 0 || opts.stage_delay_ticks < 0)
+    return fail(MK_E_INVAL, "negative option");
+  if (lq == 0 || hq == 0) {
+    if (stats != nullptr) std::memset(stats, 0, sizeof(*stats));
+    return MK_OK;  // nothing to compute
+  }
+  if (lk == 0) return fail(MK_E_INVAL, "Lk == 0: no keys to attend to");
+  if (d != 64 && d != 128) return fail(MK_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int n_steps = causal ? rank + 1 : n_chunks;
+  if (n_steps > (1 << 20) - 2) return fail(MK_E_INVAL, "too many ring steps");
+  if (lq > (1 << 30) || lk > (1 << 30) || hq > (1 << 20)) return fail(MK_E_INVAL, "extent too large");
+
+  // Decomposition.
+  mkra::KernelArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.kv = static_cast<const uint16_t*>(kv->data);
+  a.out = static_cast<uint16_t*>(out->data);
+  a.lse = static_cast<float*>(lse->data);
+  a.lq = (int)lq; a.lk = (int)lk; a.hq = (int)hq; a.hkv = (int)hkv; a.d = (int)d; a.gqa = gqa;
+  a.n_chunks = n_chunks; a.rank = rank; a.causal = causal ? 1 : 0; a.n_steps = n_steps;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  a.hg = heads_per_unit(gqa);
+  a.n_hgroups = gqa / a.hg;
+  a.bq = (mkra::kWaves / a.hg) * mkra::kRowsPerWave;
+  a.n_qblocks = (int)((lq + a.bq - 1) / a.bq);
+  const int64_t n_units = hkv * a.n_hgroups * (int64_t)a.n_qblocks;
+  if (n_units > (1 << 26)) return fail(MK_E_INVAL, "too many compute units");
+  a.n_units = (int)n_units;
+  a.n_tiles = (int)((lk + mkra::kStageRows - 1) / mkra::kStageRows);
+  a.parts_per_tile = (int)((mkra::kStageRows * hkv * d + mkra::kStagePartElems - 1) / mkra::kStagePartElems);
+  const int64_t n_stage_tasks = (int64_t)(n_steps - 1) * a.n_tiles * a.parts_per_tile;
+  if (n_stage_tasks > (int64_t)INT32_MAX - 1) return fail(MK_E_INVAL, "too many staging tasks");
+  a.n_stage_tasks = (int)n_stage_tasks;
+  a.chunk_elems = 2 * lk * hkv * d;
+
+  // Device state.
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if ((s = check_device_pointer(q->data, dev, "q")) != MK_OK) return s;
+  if ((s = check_device_pointer(kv->data, dev, "kv_chunks")) != MK_OK) return s;
+  if ((s = check_device_pointer(out->data, dev, "out")) != MK_OK) return s;
+  if ((s = check_device_pointer(lse->data, dev, "lse")) != MK_OK) return s;
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo* di = nullptr;
+  if ((s = device_info(dev, &di)) != MK_OK) return s;
+  const int capacity = di->cus * di->occ[d == 128 ? 1 : 0];
+  int grid = opts.grid_wgs > 0 ? std::min(opts.grid_wgs, capacity) : capacity;
+  // No more workgroups than tasks can use at once.
+  const int64_t useful = n_units + std::min<int64_t>(n_stage_tasks, 16);
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, useful));
+  a.grid = grid;
+  a.n_xcd = std::min(mkra::kMaxXcd, grid);
+  for (int x = 0; x <= a.n_xcd; ++x) a.xcd_unit_begin[x] = (int)((int64_t)x * n_units / a.n_xcd);
+
+  // Cost model for the controller's priors and the initial split (Eq. (2) with
+  // modelled costs; §3.2: the data dependency sets the initial allocation).
+  // Compute: a task's FLOPs at half of one CU's bf16 MFMA peak (4096 FLOP/clk at
+  // 2.4 GHz). Staging: a part's read+write bytes at 10 GB/s per wave, kWaves waves
+  // per workgroup. Ticks are 100 MHz.
+  const double task_flops = 4.0 * d * (a.hg * a.bq) * (double)lk;
+  const double cu_rate = 0.5 * 4096.0 * 2.4e9;
+  a.cost_compute0 = std::max<int64_t>(1, (int64_t)(task_flops / cu_rate * 1e8));
+  const double part_bytes = 2.0 * 2.0 * 2.0 * std::min<int64_t>(mkra::kStagePartElems, mkra::kStageRows * hkv * d);
+  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(part_bytes / 10e9 * 1e8 / mkra::kWaves));
+  a.split_fixed = opts.split_mode == MK_SPLIT_FIXED ? 1 : 0;
+  a.disable_staging = opts.disable_staging ? 1 : 0;
+  a.stage_delay_ticks = opts.stage_delay_ticks;
+  a.debug_flags = opts.debug_flags;
+  int init = 0;
+  if (n_stage_tasks > 0 && !a.disable_staging) {
+    if (a.split_fixed)
+      init = std::min(opts.fixed_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
+    else if (opts.initial_staging_wgs > 0)
+      init = std::min(opts.initial_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
+    else
+      init = eq2_target_host(grid, n_units * (int64_t)n_steps, n_stage_tasks, a.cost_compute0, a.cost_stage0);
+  }
+  a.initial_stagers = init;
+  a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;
+  a.ctrl_period_ticks = (uint64_t)(opts.controller_period_us > 0 ? opts.controller_period_us : 20) * 100ull;
+
+  Workspace* w = find_ws(dev, stream, true);
+#define GROW(field, cap, need, zero)                                                   \
+  if ((e = grow(&w->field, &cap, (size_t)(need), stream, zero)) != hipSuccess) \
+    return hip_fail(e, "workspace allocation");
+  if (w->ctrl == nullptr) {
+    if ((e = hipMalloc(reinterpret_cast<void**>(&w->ctrl), sizeof(DevCtrl))) != hipSuccess)
+      return hip_fail(e, "workspace allocation");
+    if ((e = hipMalloc(reinterpret_cast<void**>(&w->status), sizeof(DevStatus))) != hipSuccess)
+      return hip_fail(e, "workspace allocation");
+    if ((e = hipMemsetAsync(w->ctrl, 0, sizeof(DevCtrl), stream)) != hipSuccess) return hip_fail(e, "memset");
+    if ((e = hipMemsetAsync(w->status, 0, sizeof(DevStatus), stream)) != hipSuccess) return hip_fail(e, "memset");
+  }
+  GROW(done_count, w->done_cap, n_steps, true);
+  GROW(slot_flags, w->tiles_cap, 2 * (size_t)a.n_tiles, true);
+  GROW(tile_parts, w->parts_cap, 2 * (size_t)a.n_tiles, true);
+  GROW(unit_flags, w->units_cap, n_units, true);
+  if (n_steps > 1) {
+    GROW(slots, w->slot_elems_cap, 2 * (size_t)a.chunk_elems, false);
+    GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
+  }
+  if (opts.trace) {
+    size_t cap = (size_t)(opts.trace_capacity > 0 ? opts.trace_capacity : 262144);
+    size_t tc = (size_t)w->trace_cap;
+    GROW(trace, tc, cap, false);
+    w->trace_cap = (int)std::min<size_t>(tc, INT32_MAX);
+  }
+#undef GROW
+  a.slots = w->slots;
+  a.slot_flags = w->slot_flags;
+  a.tile_parts = w->tile_parts;
+  a.unit_flags = w->unit_flags;
+  a.acc = w->acc;
+  a.done_count = w->done_count;
+  a.ctrl = w->ctrl;
+  a.status = w->status;
+  a.trace = opts.trace ? w->trace : nullptr;
+  a.trace_cap = opts.trace ? w->trace_cap : 0;
+  w->traced_last = opts.trace != 0;
+  a.epoch = ++w->epoch;
+
+  if ((e = mkra_kernel_launch(&a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+
+  if (stats != nullptr) {
+    std::memset(stats, 0, sizeof(*stats));
+    DevStatus ds;
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if ((e = hipMemcpy(&ds, w->status, sizeof(ds), hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+    stats->status = (int32_t)ds.last_error;
+    stats->grid_wgs = grid;
+    stats->n_units = a.n_units;
+    stats->n_steps = n_steps;
+    stats->n_stage_tiles = a.n_tiles;
+    stats->n_stage_parts = a.n_stage_tasks;
+    stats->compute_tasks_done = ds.compute_done;
+    stats->staging_tasks_done = ds.stage_done;
+    stats->assist_tasks = ds.assist_tasks;
+    stats->initial_target = ds.initial_target;
+    stats->final_target = ds.final_target;
+    stats->max_staging_wgs = ds.max_stage;
+    stats->controller_updates = ds.ctrl_updates;
+    stats->role_switches = ds.role_switches;
+    stats->compute_busy_ticks = ds.compute_ticks;
+    stats->compute_wait_ticks = ds.compute_wait_ticks;
+    stats->staging_busy_ticks = ds.stage_ticks;
+    stats->staging_wait_ticks = ds.stage_wait_ticks;
+    stats->kernel_ticks = ds.kernel_ticks;
+    stats->trace_records = ds.trace_records;
+    stats->debug_mismatches = ds.debug_mismatch;
+  }
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void mk_ring_attn_default_opts(mk_ring_attn_opts* opts) {
+  if (opts == nullptr) return;
+  std::memset(opts, 0, sizeof(*opts));
+  opts->split_mode = MK_SPLIT_ADAPTIVE;
+}
+
+mk_status mk_ring_attn_fwd(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank, int causal,
+                           int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream) {
+  return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, nullptr, nullptr);
+}
+
+mk_status mk_ring_attn_fwd_ex(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank, int causal,
+                              int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream,
+                              const mk_ring_attn_opts* opts, mk_ring_attn_stats* stats) {
+  return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, opts, stats);
+}
+
+mk_status mk_ring_attn_status(hipStream_t stream) {
+  g_last_error.clear();
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  Workspace* w = find_ws(dev, stream, false);
+  if (w == nullptr || w->status == nullptr) return MK_OK;
+  uint32_t sticky = 0;
+  if ((e = hipMemcpy(&sticky, &w->status->sticky_error, sizeof(sticky), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  if (sticky == 0) return MK_OK;
+  const uint32_t zero = 0;
+  if ((e = hipMemcpy(&w->status->sticky_error, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  return fail(MK_E_TIMEOUT, "a bounded wait on the GPU expired (status of an earlier call on this stream)");
+}
+
+mk_status mk_ring_attn_trace(hipStream_t stream, mk_trace_record* records, int64_t capacity, int64_t* n_copied) {
+  g_last_error.clear();
+  static_assert(sizeof(mk_trace_record) == sizeof(TraceRec), "trace record layout");
+  if (n_copied == nullptr || (records == nullptr && capacity > 0) || capacity < 0)
+    return fail(MK_E_INVAL, "bad trace buffer");
+  *n_copied = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace* w = find_ws(dev, stream, false);
+  if (w == nullptr || !w->traced_last || w->trace == nullptr) return fail(MK_E_INVAL, "no traced call on stream");
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int64_t written = 0;
+  if ((e = hipMemcpy(&written, &w->status->trace_records, sizeof(written), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  int64_t n = std::min<int64_t>(std::min<int64_t>(written, w->trace_cap), capacity);
+  if (n > 0 && (e = hipMemcpy(records, w->trace, (size_t)n * sizeof(TraceRec), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy");
+  *n_copied = n;
+  return MK_OK;
+}
+
+const char* mk_last_error(void) { return g_last_error.c_str(); }
+
+void mk_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (Workspace* w : g_ws) free_ws(w);
+  g_ws.clear();
+}
+
+int mk_abi_version(void) { return MKRA_ABI_VERSION; }
+
+}  // extern "C"

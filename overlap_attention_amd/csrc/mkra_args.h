@@ -1,0 +1,145 @@
+// Shared between the host launcher and the persistent kernel: launch arguments and
+// the layout of the device-side control block. Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace mkra {
+
+// Geometry of a compute workgroup: 8 waves of 64 lanes, each wave owning 32 query
+// rows of one query head (the n index of a 32x32x16 bf16 MFMA).
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;
+// Keys per KV tile held in LDS (double-buffered).
+constexpr int kBN = 64;
+// Rows of a staged KV tile: the pages' Table 3 moves Ring Attention's KV in tiles of
+// 128 rows; one ready flag per (slot, tile).
+constexpr int kStageRows = 128;
+// Elements of K (and as many of V) copied by one staging task: a 128-row tile is cut
+// into parts of at most this size so several waves can fill one tile; the wave that
+// finishes the last part of a tile publishes its flag (a per-tile counter, as the
+// paper's §3.1 lets the last finished tile of a chunk publish readiness).
+constexpr int kStagePartElems = 16384;  // 32 KiB of K + 32 KiB of V
+constexpr int kMaxXcd = 8;
+
+enum : uint32_t { kRoleCompute = 0, kRoleStage = 1 };
+enum : uint32_t { kErrNone = 0, kErrTimeout = 4 };
+enum : int32_t { kTraceCompute = 1, kTraceStage = 2, kTraceController = 3, kTraceRole = 4 };
+
+// One counter per 64-byte line: the counters are hit by atomics from every CU.
+struct alignas(64) Line32 {
+  uint32_t v;
+  uint32_t pad[15];
+};
+struct alignas(64) Line64 {
+  uint64_t v;
+  uint64_t pad[7];
+};
+
+// Reset to zero by the last workgroup to leave each launch (and at allocation).
+struct DevCtrl {
+  Line32 xcd_head[kMaxXcd];   // compute tasks claimed from each XCD's queue
+  Line32 stage_head;          // staging tasks claimed
+  Line32 n_stage;             // workgroups currently in the staging role
+  Line32 target;              // controller's target for n_stage
+  Line32 error;               // first device-side error of this launch
+  Line32 exit_count;          // workgroups that have left the loop
+  Line64 ctrl_time;           // tick of the last controller update
+  Line64 compute_ticks;       // busy ticks of finished compute tasks
+  Line32 compute_done;
+  Line64 stage_ticks;         // busy ticks of finished staging tasks (per wave)
+  Line32 stage_done;
+  Line64 compute_wait_ticks;
+  Line64 stage_wait_ticks;
+  Line32 assist_tasks;
+  Line32 ctrl_updates;
+  Line32 role_switches;
+  Line32 max_stage;
+  Line32 trace_head;
+  Line32 debug_mismatch;      // debug: staged vectors that differed from their source
+  Line64 t_first;             // min start tick (0 = unset)
+  Line64 t_last;              // max exit tick
+};
+
+// Survives launches: the host reads it after a call.
+struct DevStatus {
+  uint32_t sticky_error;      // OR of device errors since the host last cleared it
+  uint32_t last_error;        // error of the last launch
+  int32_t initial_target;
+  int32_t final_target;
+  int32_t compute_done;
+  int32_t stage_done;
+  int32_t assist_tasks;
+  int32_t ctrl_updates;
+  int32_t role_switches;
+  int32_t max_stage;
+  int64_t compute_ticks;
+  int64_t compute_wait_ticks;
+  int64_t stage_ticks;
+  int64_t stage_wait_ticks;
+  int64_t kernel_ticks;
+  int64_t trace_records;
+  int64_t debug_mismatch;
+};
+
+struct TraceRec {
+  uint64_t t;
+  int32_t wg;
+  int32_t kind;
+  int64_t v[6];
+};
+
+struct KernelArgs {
+  // Problem (device pointers into caller-owned tensors).
+  const uint16_t* q;      // [Lq, Hq, D] bf16
+  const uint16_t* kv;     // [N, 2, Lk, Hkv, D] bf16
+  uint16_t* out;          // [Lq, Hq, D] bf16
+  float* lse;             // [Hq, Lq] fp32
+  int lq, lk, hq, hkv, d, gqa;
+  int n_chunks, rank, causal, n_steps;
+  float scale_log2;       // log2(e) / sqrt(D)
+
+  // Decomposition into compute units: a unit is (KV head, group of HG query heads
+  // sharing it, block of BQ query rows); its 8 waves are HG heads x (BQ/32) row blocks.
+  int hg;                 // query heads per unit
+  int n_hgroups;          // G / hg
+  int bq;                 // query rows per unit
+  int n_qblocks;          // ceil(Lq / bq)
+  int n_units;
+  int n_xcd;              // compute queues (one per XCD)
+  int xcd_unit_begin[kMaxXcd + 1];
+
+  // Staging work: tasks = (step 1..S-1) x (tile) x (part).
+  int n_tiles;            // ceil(Lk / 128)
+  int parts_per_tile;     // for a full 128-row tile
+  int n_stage_tasks;
+  int64_t chunk_elems;    // 2 * Lk * Hkv * D
+
+  // Workspace (library-owned device memory).
+  uint16_t* slots;        // [2][2][Lk][Hkv][D] bf16
+  uint64_t* slot_flags;   // [2][n_tiles] epoch-stamped ready flags
+  uint32_t* tile_parts;   // [2][n_tiles] parts finished (reset by the publisher)
+  uint64_t* unit_flags;   // [n_units] epoch-stamped "step done" per unit
+  float* acc;             // [n_units][kWaves][32*D + 256] running (O, m, l, lr) between steps
+  uint32_t* done_count;   // [n_steps] units finished per step (slot release)
+  DevCtrl* ctrl;
+  DevStatus* status;
+  TraceRec* trace;
+  int trace_cap;
+  uint64_t epoch;         // distinct per launch on this workspace, >= 1
+
+  // Scheduling.
+  int grid;
+  int split_fixed;        // 1 = FIXED split
+  int initial_stagers;
+  int disable_staging;
+  int stage_delay_ticks;
+  int debug_flags;        // bit 0: compute verifies staged tiles; bit 1: one staging task per round
+  int64_t cost_compute0;  // modelled ticks per compute task (controller prior)
+  int64_t cost_stage0;    // modelled ticks per staging task per workgroup
+  uint64_t timeout_ticks;
+  uint64_t ctrl_period_ticks;
+};
+
+}  // namespace mkra

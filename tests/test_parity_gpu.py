@@ -1,0 +1,288 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle, on one GPU.
+
+Every case prints what it runs before launching, so a failing GPU run names its case.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import overlap_attention_amd as mk
+from ring_inputs import CONFIGS, RingConfig, make_inputs, to_f64
+from tests.parity import compare, fmt, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# Every on-GPU wait is bounded well below the test timeout.
+TEST_TIMEOUT_US = 5_000_000
+
+
+def opts(**kw):
+    kw.setdefault("spin_timeout_us", TEST_TIMEOUT_US)
+    return mk.default_opts(**kw)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def run_gpu(q, kv, cfg, **kw):
+    want_stats = kw.pop("want_stats", False)
+    res = mk.ring_attn_fwd(q, kv, cfg.rank, cfg.causal, cfg.gqa_ratio, opts=opts(**kw), want_stats=want_stats)
+    torch.cuda.synchronize()
+    mk.mk_ring_attn_status()
+    return res
+
+
+def check_full(cfg, seed, **kw):
+    announce(f"{cfg} seed={seed} opts={kw}")
+    q, kv = make_inputs(cfg, seed)
+    qg, kvg = q.cuda(), kv.cuda()
+    out, lse = run_gpu(qg, kvg, cfg, **kw)
+    ref_o, ref_l = oracle.ring_attention_reference(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio)
+    rep = compare(to_f64(out), lse.double().cpu().numpy(), ref_o, ref_l)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
+    return out, lse
+
+
+def shape(name, n, rank, lq, lk, hq, hkv, d, causal, qk_mult=1.0):
+    return RingConfig(name, rank=rank, n_chunks=n, lq=lq, lk=lk, hq=hq, hkv=hkv, d=d, causal=causal,
+                      qk_mult=qk_mult)
+
+
+# --------------------------------------------------------------- the five workloads
+
+def test_tiny_workload_full():
+    check_full(CONFIGS[0], seed=0)
+
+
+SMALL_SHAPES = [
+    shape("single_key", 1, 0, 1, 1, 1, 1, 64, True),
+    shape("one_row_many_steps", 5, 4, 1, 1, 2, 1, 128, True),
+    shape("ragged_causal_g2", 3, 1, 200, 200, 6, 3, 64, True),
+    shape("ragged_noncausal_g2", 3, 2, 200, 200, 6, 3, 64, False),
+    shape("lq_ne_lk_g3", 2, 0, 77, 300, 6, 2, 128, False),
+    shape("g16_ragged", 4, 3, 129, 129, 16, 1, 128, True),
+    shape("d64_two_blocks", 2, 1, 513, 513, 8, 8, 64, True),
+    shape("g8_noncausal", 6, 2, 384, 384, 8, 1, 128, False),
+    shape("short_q_long_k", 3, 0, 64, 1000, 4, 2, 64, False),
+    shape("rank0_causal", 4, 0, 256, 256, 4, 4, 128, True),
+    shape("g4_causal_tail", 3, 2, 320, 320, 8, 2, 128, True, qk_mult=2.0),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_SHAPES, ids=lambda c: c.name)
+def test_small_shapes_full(cfg):
+    check_full(cfg, seed=11)
+
+
+def test_small_workload_full():
+    check_full(CONFIGS[1], seed=1)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4], ids=lambda i: CONFIGS[i].name)
+def test_full_size_workloads_sampled(idx):
+    """Full shapes in the default launch configuration (as benchmarked); the oracle
+    evaluates sampled query rows of every head."""
+    cfg = CONFIGS[idx]
+    announce(f"{cfg} seed={idx} sampled")
+    q, kv = make_inputs(cfg, seed=idx)
+    qg, kvg = q.cuda(), kv.cuda()
+    out, lse, stats = run_gpu(qg, kvg, cfg, want_stats=True)
+    print("    stats:", stats, flush=True)
+    rows = sample_rows(cfg.lq, n_random=24, seed=idx)
+    ref_o, ref_l = oracle.ring_attention_rows(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio, rows)
+    rep = compare(to_f64(out[rows]), lse[:, rows].double().cpu().numpy(), ref_o, ref_l)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert stats["status"] == 0
+    assert stats["compute_tasks_done"] == stats["n_units"] * stats["n_steps"]
+    assert stats["staging_tasks_done"] == stats["n_stage_parts"]
+
+
+SPLIT_VARIANTS = [
+    dict(),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=0),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=2),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, stage_delay_ticks=3000),
+    dict(grid_wgs=1),
+    dict(grid_wgs=2),
+    dict(grid_wgs=8),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, debug_flags=7),
+]
+
+
+@pytest.mark.parametrize("variant", SPLIT_VARIANTS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v) or "default")
+def test_many_steps_every_split_matches_oracle(variant):
+    """Six ring steps, slots reused three times, one or many staging workgroups."""
+    cfg = shape("g8_noncausal", 6, 2, 384, 384, 8, 1, 128, False)
+    for rep in range(3):
+        out, lse = check_full(cfg, seed=11, **variant)
+    if variant.get("debug_flags"):
+        q, kv = make_inputs(cfg, seed=11)
+        st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, **variant)[2]
+        assert st["debug_mismatches"] == 0, st
+
+
+# --------------------------------------------------------------- special cases
+
+def test_constant_v_rows_return_v():
+    cfg = shape("constv", 4, 2, 256, 256, 8, 2, 128, True)
+    announce("constant V")
+    q, kv = make_inputs(cfg, seed=3)
+    u = torch.randn((cfg.hkv, cfg.d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    kv[:, 1] = u[None, None]
+    out, _ = run_gpu(q.cuda(), kv.cuda(), cfg)
+    want = u.double().repeat_interleave(cfg.gqa_ratio, dim=0)[None].expand(cfg.lq, -1, -1)
+    err = (out.double().cpu() - want).abs().max().item()
+    print("    max err", err, flush=True)
+    assert err <= 1e-2
+
+
+def test_future_chunks_never_read():
+    cfg = shape("poison", 6, 2, 192, 192, 4, 2, 64, True)
+    announce("causal poisoning of chunks after the rank")
+    q, kv = make_inputs(cfg, seed=4)
+    o1, l1 = run_gpu(q.cuda(), kv.cuda(), cfg)
+    bad = kv.clone()
+    bad[cfg.rank + 1:] = float("nan")
+    o2, l2 = run_gpu(q.cuda(), bad.cuda(), cfg)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_noncausal_rank_invariance():
+    base = shape("rankinv", 4, 0, 128, 128, 4, 4, 64, False)
+    q, kv = make_inputs(base, seed=6)
+    announce("non-causal rank invariance")
+    outs = []
+    for r in range(4):
+        cfg = shape("rankinv", 4, r, 128, 128, 4, 4, 64, False)
+        outs.append(run_gpu(q.cuda(), kv.cuda(), cfg))
+    for o, l in outs[1:]:
+        assert (o.float() - outs[0][0].float()).abs().max().item() <= 1e-2
+        assert ((l - outs[0][1]).abs() / outs[0][1].abs().clamp(min=1)).max().item() <= 1e-3
+
+
+# --------------------------------------------------------------- protocol
+
+def test_bitwise_identical_across_splits_grids_and_delays():
+    cfg = CONFIGS[1]
+    q, kv = make_inputs(cfg, seed=1)
+    qg, kvg = q.cuda(), kv.cuda()
+    announce("reference split")
+    ref_o, ref_l = check_full(cfg, seed=1)
+    variants = [dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n) for n in (0, 1, 2, 4, 8, 32)]
+    variants += [dict(grid_wgs=g) for g in (1, 3, 8, 37)]
+    variants += [dict(stage_delay_ticks=2000), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+                                                   stage_delay_ticks=5000)]
+    variants += [dict(initial_staging_wgs=16, controller_period_us=1)]
+    for v in variants:
+        announce(f"variant {v}")
+        o, l = run_gpu(qg, kvg, cfg, **v)
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), v
+
+
+def test_back_to_back_launches_and_shape_changes():
+    a = CONFIGS[1]
+    b = shape("other", 5, 3, 300, 300, 8, 2, 64, True)
+    qa, kva = make_inputs(a, seed=21)
+    qb, kvb = make_inputs(b, seed=22)
+    ra = oracle.ring_attention_reference(to_f64(qa), to_f64(kva), a.rank, a.causal, a.gqa_ratio)
+    rb = oracle.ring_attention_reference(to_f64(qb), to_f64(kvb), b.rank, b.causal, b.gqa_ratio)
+    qa, kva, qb, kvb = qa.cuda(), kva.cuda(), qb.cuda(), kvb.cuda()
+    plan = [(a, qa, kva, ra), (b, qb, kvb, rb), (a, qa, kva, ra), (a, qa, kva, ra)]
+    results = []
+    for i, (cfg, q, kv, _) in enumerate(plan):
+        announce(f"launch {i}: {cfg.name}")
+        # Enqueued back to back on one stream: the launches share one workspace.
+        results.append(mk.ring_attn_fwd(q, kv, cfg.rank, cfg.causal, cfg.gqa_ratio, opts=opts()))
+    torch.cuda.synchronize()
+    mk.mk_ring_attn_status()
+    for i, ((out, lse), (_, _, _, ref)) in enumerate(zip(results, plan)):
+        rep = compare(to_f64(out), lse.double().cpu().numpy(), *ref)
+        assert rep["ok"], (i, fmt(rep))
+
+
+def test_stale_slots_of_previous_launch_are_not_consumed():
+    """Launch with inputs X, then with inputs Y and slow staging: a compute wave that
+    consumed a flag of the earlier launch would read X's chunks from the slots."""
+    cfg = shape("stale", 6, 5, 256, 256, 8, 4, 128, True)
+    qx, kvx = make_inputs(cfg, seed=31)
+    qy, kvy = make_inputs(cfg, seed=32)
+    ref = oracle.ring_attention_reference(to_f64(qy), to_f64(kvy), cfg.rank, cfg.causal, cfg.gqa_ratio)
+    qx, kvx, qy, kvy = qx.cuda(), kvx.cuda(), qy.cuda(), kvy.cuda()
+    announce("stale slot check")
+    mk.ring_attn_fwd(qx, kvx, cfg.rank, cfg.causal, cfg.gqa_ratio, opts=opts())
+    out, lse = mk.ring_attn_fwd(qy, kvy, cfg.rank, cfg.causal, cfg.gqa_ratio,
+                                opts=opts(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+                                          stage_delay_ticks=20000))
+    torch.cuda.synchronize()
+    mk.mk_ring_attn_status()
+    rep = compare(to_f64(out), lse.double().cpu().numpy(), *ref)
+    assert rep["ok"], fmt(rep)
+
+
+def test_wait_bound_reports_timeout_and_recovers():
+    cfg = shape("timeout", 3, 2, 128, 128, 2, 2, 64, True)
+    q, kv = make_inputs(cfg, seed=41)
+    qg, kvg = q.cuda(), kv.cuda()
+    announce("staging disabled: the bounded waits must expire")
+    mk.ring_attn_fwd(qg, kvg, cfg.rank, cfg.causal, cfg.gqa_ratio,
+                     opts=mk.default_opts(disable_staging=1, spin_timeout_us=100_000))
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_ring_attn_status()
+    assert e.value.status == mk.MK_E_TIMEOUT
+    announce("next call on the same workspace")
+    check_full(cfg, seed=41)
+
+
+def test_stats_and_controller_follow_eq2():
+    cfg = CONFIGS[1]
+    q, kv = make_inputs(cfg, seed=1)
+    announce("traced adaptive run")
+    out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2)
+    print("    stats:", st, flush=True)
+    assert st["status"] == 0
+    assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]
+    assert st["staging_tasks_done"] == st["n_stage_parts"]
+    recs = mk.mk_ring_attn_trace()
+    ctrl = [r for r in recs if r[2] == 3]
+    comp = [r for r in recs if r[2] == 1]
+    stage = [r for r in recs if r[2] == 2]
+    assert len(comp) == st["compute_tasks_done"] and len(stage) == st["staging_tasks_done"]
+    assert len(ctrl) == st["controller_updates"] and len(ctrl) >= 1
+    for r in ctrl:
+        rp, rs, cp, cs, b, target = r[3:9]
+        exact = oracle.controller_target(b, rp, rs, cp, cs)
+        # The kernel's integer rounding (half up) and clamp to [1, min(B-1, Rs)].
+        if rs <= 0:
+            want = 0
+        else:
+            hi = min(b - 1, rs)
+            want = max(min(1, hi), min(hi, math.floor(exact + 0.5)))
+        # Exact ties are decided in integers by the kernel; the float may sit a hair off.
+        assert target == want or abs(exact + 0.5 - round(exact + 0.5)) < 1e-9, (r, exact)
+    # Every (unit, step) ran once, finishing in step order per unit.
+    seen = {}
+    for r in sorted(comp, key=lambda r: r[0]):
+        unit, step = r[3], r[4]
+        assert seen.get(unit, -1) == step - 1
+        seen[unit] = step
+    assert len(seen) == st["n_units"]
+
+
+def test_host_pointer_rejected():
+    cfg = shape("hostptr", 2, 1, 128, 128, 2, 2, 64, True)
+    q, kv = make_inputs(cfg, seed=51)
+    out = torch.empty_like(q).cuda()
+    lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device="cuda")
+    announce("host pointer")
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_ring_attn_fwd(q, kv.cuda(), cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, out, lse)
+    assert e.value.status == mk.MK_E_INVAL
