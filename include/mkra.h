@@ -12,9 +12,10 @@
  *
  * Everything runs in ONE persistent kernel per call. Its workgroups (one per compute
  * unit) take one of two roles: compute (the attention steps) or staging (the ring
- * receive: copy the next KV chunk into a double buffer in HBM, 128-row tile by
- * 128-row tile, publishing an epoch-stamped ready flag per tile). An on-GPU
- * controller re-targets the number of staging workgroups with Eq. (2).
+ * receive: copy each step's KV chunk into a double buffer in HBM, 128-row tile by
+ * 128-row tile, in the layout the compute role reads, and publish an epoch-stamped
+ * ready flag per tile). An on-GPU controller re-targets the number of staging
+ * workgroups with Eq. (2).
  *
  * Conventions for every entry point:
  *  - All tensor data pointers are DEVICE pointers on the current HIP device; every
@@ -80,17 +81,17 @@ typedef struct {
   int32_t controller_period_us;/* minimum time between controller updates; 0 = 20 us. */
   int32_t trace;               /* nonzero: record per-task events (mk_ring_attn_trace). */
   int32_t trace_capacity;      /* records kept when tracing; 0 = 262144. */
-  int32_t disable_staging;     /* DEBUG: nobody stages, so every step after the first
+  int32_t disable_staging;     /* DEBUG: nobody stages, so the first compute task
                                   waits until spin_timeout_us and the call reports
                                   MK_E_TIMEOUT. All workgroups still exit normally. */
-  int32_t stage_delay_ticks;   /* DEBUG: before publishing each staged part, spin a
+  int32_t stage_delay_ticks;   /* DEBUG: before publishing each staged tile, spin a
                                   pseudo-random 0..stage_delay_ticks (100 MHz ticks). */
-  int32_t debug_flags;         /* DEBUG bit mask, 0 in normal use. bit 0: compute waves
-                                  compare every staged vector they load with the
-                                  chunk's home copy; bit 1: a staging wave runs one
-                                  task per round; bit 2: a staging wave reads back what
-                                  it copied. Mismatches are counted in
-                                  mk_ring_attn_stats.debug_mismatches. */
+  int32_t debug_flags;         /* DEBUG bit mask, 0 in normal use. bit 0: a staging
+                                  workgroup reads back the K part of every block it
+                                  wrote and compares it with the chunk's home copy;
+                                  mismatches are counted in
+                                  mk_ring_attn_stats.debug_mismatches. Other bits are
+                                  ignored. */
   int32_t reserved[5];
 } mk_ring_attn_opts;
 
@@ -102,9 +103,10 @@ typedef struct {
   int32_t n_units;             /* compute units per step (head group x query block) */
   int32_t n_steps;             /* ring steps run */
   int32_t n_stage_tiles;       /* 128-row staged tiles per chunk */
-  int32_t n_stage_parts;       /* staging tasks in total (parts of tiles, all steps) */
+  int32_t n_stage_tasks;       /* staging tasks in total: one per (step, tile); the
+                                  local chunk of step 0 is staged too */
   int32_t compute_tasks_done;
-  int32_t staging_tasks_done;  /* by staging workgroups and by stalled compute waves */
+  int32_t staging_tasks_done;  /* by staging and by compute workgroups */
   int32_t assist_tasks;        /* staging tasks done by compute workgroups whose input
                                   was not ready (the stall rule of §3.2) */
   int32_t initial_target;      /* staging workgroups at launch */
@@ -114,12 +116,11 @@ typedef struct {
   int32_t role_switches;
   int64_t compute_busy_ticks;  /* summed over compute tasks, waits excluded */
   int64_t compute_wait_ticks;  /* compute waves waiting on ready flags / unit order */
-  int64_t staging_busy_ticks;  /* summed over staging tasks (per wave), waits excluded */
-  int64_t staging_wait_ticks;  /* staging waves waiting for a slot to be released */
+  int64_t staging_busy_ticks;  /* summed over staging tasks, waits excluded */
+  int64_t staging_wait_ticks;  /* staging workgroups waiting for a slot to be released */
   int64_t kernel_ticks;        /* first workgroup start to last workgroup exit */
   int64_t trace_records;       /* records written (may exceed trace_capacity) */
-  int64_t debug_mismatches;    /* see mk_ring_attn_opts.debug_flags (readback count in
-                                  bits 16+, load-time count in bits 0-15) */
+  int64_t debug_mismatches;    /* see mk_ring_attn_opts.debug_flags */
   int64_t reserved[3];
 } mk_ring_attn_stats;
 

@@ -54,7 +54,7 @@ class mk_ring_attn_stats(ctypes.Structure):
         ("n_units", ctypes.c_int32),
         ("n_steps", ctypes.c_int32),
         ("n_stage_tiles", ctypes.c_int32),
-        ("n_stage_parts", ctypes.c_int32),
+        ("n_stage_tasks", ctypes.c_int32),
         ("compute_tasks_done", ctypes.c_int32),
         ("staging_tasks_done", ctypes.c_int32),
         ("assist_tasks", ctypes.c_int32),

@@ -47,12 +47,10 @@ struct Workspace {
   size_t done_cap = 0;
   uint64_t* slot_flags = nullptr;
   size_t tiles_cap = 0;
-  uint32_t* tile_parts = nullptr;
-  size_t parts_cap = 0;
   uint64_t* unit_flags = nullptr;
   size_t units_cap = 0;
-  uint16_t* slots = nullptr;
-  size_t slot_elems_cap = 0;
+  uint8_t* slots = nullptr;
+  size_t slot_bytes_cap = 0;
   float* acc = nullptr;
   size_t acc_cap = 0;
   TraceRec* trace = nullptr;
@@ -96,7 +94,6 @@ void free_ws(Workspace* w) {
     hipFree(w->status);
     hipFree(w->done_count);
     hipFree(w->slot_flags);
-    hipFree(w->tile_parts);
     hipFree(w->unit_flags);
     hipFree(w->slots);
     hipFree(w->acc);
@@ -263,11 +260,15 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   if (n_units > (1 << 26)) return fail(MK_E_INVAL, "too many compute units");
   a.n_units = (int)n_units;
   a.n_tiles = (int)((lk + mkra::kStageRows - 1) / mkra::kStageRows);
-  a.parts_per_tile = (int)((mkra::kStageRows * hkv * d + mkra::kStagePartElems - 1) / mkra::kStagePartElems);
-  const int64_t n_stage_tasks = (int64_t)(n_steps - 1) * a.n_tiles * a.parts_per_tile;
+  a.n_blocks = (int)((lk + mkra::kBN - 1) / mkra::kBN);
+  // Every step's chunk, the local one included, is staged once into the layout the
+  // compute role reads.
+  const int64_t n_stage_tasks = (int64_t)n_steps * a.n_tiles;
   if (n_stage_tasks > (int64_t)INT32_MAX - 1) return fail(MK_E_INVAL, "too many staging tasks");
   a.n_stage_tasks = (int)n_stage_tasks;
   a.chunk_elems = 2 * lk * hkv * d;
+  const int64_t block_bytes = 2 * (int64_t)mkra::kBN * d * 2;
+  a.slot_bytes = hkv * (int64_t)a.n_blocks * block_bytes;
 
   // Device state.
   int dev = 0;
@@ -293,13 +294,13 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   // Cost model for the controller's priors and the initial split (Eq. (2) with
   // modelled costs; §3.2: the data dependency sets the initial allocation).
   // Compute: a task's FLOPs at half of one CU's bf16 MFMA peak (4096 FLOP/clk at
-  // 2.4 GHz). Staging: a part's read+write bytes at 10 GB/s per wave, kWaves waves
-  // per workgroup. Ticks are 100 MHz.
+  // 2.4 GHz). Staging: a tile's read+write bytes at 40 GB/s per workgroup. Ticks are
+  // 100 MHz.
   const double task_flops = 4.0 * d * (a.hg * a.bq) * (double)lk;
   const double cu_rate = 0.5 * 4096.0 * 2.4e9;
   a.cost_compute0 = std::max<int64_t>(1, (int64_t)(task_flops / cu_rate * 1e8));
-  const double part_bytes = 2.0 * 2.0 * 2.0 * std::min<int64_t>(mkra::kStagePartElems, mkra::kStageRows * hkv * d);
-  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(part_bytes / 10e9 * 1e8 / mkra::kWaves));
+  const double tile_bytes = 2.0 * 2.0 * 2.0 * (double)std::min<int64_t>(mkra::kStageRows, lk) * hkv * d;
+  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(tile_bytes / 40e9 * 1e8));
   a.split_fixed = opts.split_mode == MK_SPLIT_FIXED ? 1 : 0;
   a.disable_staging = opts.disable_staging ? 1 : 0;
   a.stage_delay_ticks = opts.stage_delay_ticks;
@@ -331,12 +332,9 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   }
   GROW(done_count, w->done_cap, n_steps, true);
   GROW(slot_flags, w->tiles_cap, 2 * (size_t)a.n_tiles, true);
-  GROW(tile_parts, w->parts_cap, 2 * (size_t)a.n_tiles, true);
   GROW(unit_flags, w->units_cap, n_units, true);
-  if (n_steps > 1) {
-    GROW(slots, w->slot_elems_cap, 2 * (size_t)a.chunk_elems, false);
-    GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
-  }
+  GROW(slots, w->slot_bytes_cap, 2 * (size_t)a.slot_bytes, false);
+  if (n_steps > 1) GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
   if (opts.trace) {
     size_t cap = (size_t)(opts.trace_capacity > 0 ? opts.trace_capacity : 262144);
     size_t tc = (size_t)w->trace_cap;
@@ -346,7 +344,6 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
 #undef GROW
   a.slots = w->slots;
   a.slot_flags = w->slot_flags;
-  a.tile_parts = w->tile_parts;
   a.unit_flags = w->unit_flags;
   a.acc = w->acc;
   a.done_count = w->done_count;
@@ -370,7 +367,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     stats->n_units = a.n_units;
     stats->n_steps = n_steps;
     stats->n_stage_tiles = a.n_tiles;
-    stats->n_stage_parts = a.n_stage_tasks;
+    stats->n_stage_tasks = a.n_stage_tasks;
     stats->compute_tasks_done = ds.compute_done;
     stats->staging_tasks_done = ds.stage_done;
     stats->assist_tasks = ds.assist_tasks;

@@ -14,14 +14,26 @@ constexpr int kRowsPerWave = 32;
 // Keys per KV tile held in LDS (double-buffered).
 constexpr int kBN = 64;
 // Rows of a staged KV tile: the pages' Table 3 moves Ring Attention's KV in tiles of
-// 128 rows; one ready flag per (slot, tile).
+// 128 rows; one staging task and one ready flag per (slot, tile).
 constexpr int kStageRows = 128;
-// Elements of K (and as many of V) copied by one staging task: a 128-row tile is cut
-// into parts of at most this size so several waves can fill one tile; the wave that
-// finishes the last part of a tile publishes its flag (a per-tile counter, as the
-// paper's §3.1 lets the last finished tile of a chunk publish readiness).
-constexpr int kStagePartElems = 16384;  // 32 KiB of K + 32 KiB of V
+// LDS pipeline depth of the compute role: KV blocks in flight per workgroup.
+constexpr int kStages = 4;
 constexpr int kMaxXcd = 8;
+
+// A staged KV block: the keys [64*kt, 64*kt + 64) of one KV head, laid out as the
+// compute role's LDS wants them, so a block moves into LDS as one contiguous copy.
+//   K part:   64 rows x D bf16; 16-byte chunk c of row r stored at chunk swz_k(r, c).
+//   V^T part: D rows x 64 fp16 (V transposed, keys permuted within each 16 so a lane's
+//             eight P^T values meet eight contiguous V^T values); chunk c of row d
+//             stored at chunk c ^ ((d >> 1) & 7).
+// The swizzles make the compute role's 16-byte LDS reads bank-conflict free.
+template <int D>
+struct Block {
+  static constexpr int kKBytes = kBN * D * 2;
+  static constexpr int kBytes = 2 * kKBytes;
+  static constexpr int kChunks = kBytes / 16;
+  static constexpr int kChunksPerThread = kChunks / kThreads;
+};
 
 enum : uint32_t { kRoleCompute = 0, kRoleStage = 1 };
 enum : uint32_t { kErrNone = 0, kErrTimeout = 4 };
@@ -48,7 +60,7 @@ struct DevCtrl {
   Line64 ctrl_time;           // tick of the last controller update
   Line64 compute_ticks;       // busy ticks of finished compute tasks
   Line32 compute_done;
-  Line64 stage_ticks;         // busy ticks of finished staging tasks (per wave)
+  Line64 stage_ticks;         // busy ticks of finished staging tasks
   Line32 stage_done;
   Line64 compute_wait_ticks;
   Line64 stage_wait_ticks;
@@ -110,16 +122,17 @@ struct KernelArgs {
   int n_xcd;              // compute queues (one per XCD)
   int xcd_unit_begin[kMaxXcd + 1];
 
-  // Staging work: tasks = (step 1..S-1) x (tile) x (part).
+  // Staging work: tasks = (step 0..S-1) x (128-row tile); each step's chunk is staged
+  // into slot step % 2 as blocks of 64 keys per KV head.
   int n_tiles;            // ceil(Lk / 128)
-  int parts_per_tile;     // for a full 128-row tile
+  int n_blocks;           // ceil(Lk / 64): blocks per KV head
   int n_stage_tasks;
-  int64_t chunk_elems;    // 2 * Lk * Hkv * D
+  int64_t chunk_elems;    // 2 * Lk * Hkv * D: one chunk in kv_chunks
+  int64_t slot_bytes;     // Hkv * n_blocks * block bytes
 
   // Workspace (library-owned device memory).
-  uint16_t* slots;        // [2][2][Lk][Hkv][D] bf16
+  uint8_t* slots;         // [2][Hkv][n_blocks] staged blocks
   uint64_t* slot_flags;   // [2][n_tiles] epoch-stamped ready flags
-  uint32_t* tile_parts;   // [2][n_tiles] parts finished (reset by the publisher)
   uint64_t* unit_flags;   // [n_units] epoch-stamped "step done" per unit
   float* acc;             // [n_units][kWaves][32*D + 256] running (O, m, l, lr) between steps
   uint32_t* done_count;   // [n_steps] units finished per step (slot release)
@@ -135,9 +148,9 @@ struct KernelArgs {
   int initial_stagers;
   int disable_staging;
   int stage_delay_ticks;
-  int debug_flags;        // bit 0: compute verifies staged tiles; bit 1: one staging task per round
+  int debug_flags;        // bit 0: a staging workgroup reads back the K it wrote
   int64_t cost_compute0;  // modelled ticks per compute task (controller prior)
-  int64_t cost_stage0;    // modelled ticks per staging task per workgroup
+  int64_t cost_stage0;    // modelled ticks per staging task (one tile)
   uint64_t timeout_ticks;
   uint64_t ctrl_period_ticks;
 };

@@ -19,6 +19,8 @@
 // B = P^T straight from registers).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "mkra_args.h"
 
 namespace mkra {
@@ -39,11 +41,19 @@ constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
 
-enum : int32_t { kOpExit = 0, kOpCompute = 1, kOpStage = 2, kOpAssist = 3 };
+enum : int32_t { kOpExit = 0, kOpCompute = 1, kOpStage = 2 };
 
 // ------------------------------------------------------------------ primitives
 
 __device__ __forceinline__ uint64_t ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// The launch arguments where the dispatcher placed them (the kernarg segment, where
+// the by-value KernelArgs parameter is the first argument). Out-of-line functions
+// read them through this pointer, so the by-value parameter is never address-taken
+// and never copied to scratch memory.
+__device__ __forceinline__ const KernelArgs* kernel_args() {
+  return (const KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
 
 __device__ __forceinline__ uint32_t ld32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -98,8 +108,9 @@ __device__ __forceinline__ int chunk_of_step(const KernelArgs& a, int t) {
   return c < 0 ? c + a.n_chunks : c;
 }
 
-__device__ __noinline__ void trace_rec(const KernelArgs& a, int kind, int64_t v0, int64_t v1, int64_t v2, int64_t v3,
+__device__ __noinline__ void trace_rec(const KernelArgs* ap, int kind, int64_t v0, int64_t v1, int64_t v2, int64_t v3,
                           int64_t v4, int64_t v5) {
+  const KernelArgs& a = *ap;
   if (a.trace == nullptr) return;
   uint32_t i = add32(&a.ctrl->trace_head.v, 1);
   if ((int64_t)i >= a.trace_cap) return;
@@ -146,7 +157,8 @@ __device__ int64_t compute_claimed(const KernelArgs& a) {
 }
 
 // Run by one lane. Rate-limited by a compare-and-swap on the update time.
-__device__ __noinline__ void maybe_controller(const KernelArgs& a) {
+__device__ __noinline__ void maybe_controller(const KernelArgs* ap) {
+  const KernelArgs& a = *ap;
   if (a.split_fixed || a.disable_staging) return;
   uint64_t now = ticks();
   uint64_t last = ld64(&a.ctrl->ctrl_time.v);
@@ -157,16 +169,14 @@ __device__ __noinline__ void maybe_controller(const KernelArgs& a) {
   int64_t rp = (int64_t)a.n_units * a.n_steps - compute_claimed(a);
   uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
   uint64_t sd = ld32(&a.ctrl->stage_done.v), stt = ld64(&a.ctrl->stage_ticks.v);
-  // A staging workgroup runs kWaves staging tasks at once (one per wave), so its
-  // cost per task is the per-wave cost divided by kWaves.
   int64_t cp = cd ? (int64_t)(ct / cd) : a.cost_compute0;
-  int64_t cs = sd ? (int64_t)(stt / sd / kWaves) : a.cost_stage0;
+  int64_t cs = sd ? (int64_t)(stt / sd) : a.cost_stage0;
   if (cp < 1) cp = 1;
   if (cs < 1) cs = 1;
   int n = eq2_target(a.grid, rp, rs, cp, cs);
   st32(&a.ctrl->target.v, (uint32_t)(n + 1));
   add32(&a.ctrl->ctrl_updates.v, 1);
-  trace_rec(a, kTraceController, rp, rs, cp, cs, a.grid, n);
+  trace_rec(ap, kTraceController, rp, rs, cp, cs, a.grid, n);
 }
 
 // ------------------------------------------------------------------ waits
@@ -210,125 +220,212 @@ __device__ bool wave_wait_stamp(const KernelArgs& a, const uint64_t* p, uint64_t
   return ok;
 }
 
-// ------------------------------------------------------------------ staging role
+// ------------------------------------------------------------------ LDS
 
-// One staging task, run by one wave: part `part` of 128-row tile `j` of the chunk of
-// step t, copied from the chunk's home (kv_chunks, standing for the predecessor's
-// memory) into slot t % 2. The slot is free once every unit has finished step t-2.
-// The wave that completes the last part of the tile publishes its flag.
-__device__ __forceinline__ bool stage_task(const KernelArgs& a, uint32_t k, bool assist, uint64_t& waited) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t t_begin = ticks();
-  const int per_step = a.n_tiles * a.parts_per_tile;
-  const int t = 1 + (int)k / per_step;
-  const int rem = (int)k % per_step;
-  const int j = rem / a.parts_per_tile;
-  const int part = rem % a.parts_per_tile;
-  const int slot = t & 1;
-  uint64_t w = 0;
-  bool ok = true;
-  int64_t dst_off = -1;
-  if (t >= 2) ok = wave_wait_ge32(a, &a.done_count[t - 2], (uint32_t)a.n_units, w);
+typedef __attribute__((address_space(3))) void lds_void;
 
-  if (ok) {
-    const int c = chunk_of_step(a, t);
-    const int r0 = j * kStageRows;
-    const int nr = min(kStageRows, a.lk - r0);
-    const int64_t row_elems = (int64_t)a.hkv * a.d;
-    const int64_t tile_elems = (int64_t)nr * row_elems;
-    const int64_t e0 = (int64_t)part * kStagePartElems;
-    const int64_t e1 = min(tile_elems, e0 + (int64_t)kStagePartElems);
-    const int64_t half = (int64_t)a.lk * row_elems;
-    const int64_t off = (int64_t)r0 * row_elems + e0;
-    const uint16_t* src = a.kv + (int64_t)c * a.chunk_elems + off;
-    uint16_t* dst = a.slots + (int64_t)slot * a.chunk_elems + off;
-    const int64_t n16 = e1 > e0 ? (e1 - e0) / 8 : 0;  // 16-byte vectors of K (and of V)
-    // K then V, 8 vectors in flight per lane.
-    for (int kvsel = 0; kvsel < 2; ++kvsel) {
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(src + kvsel * half);
-      u32x4* d4 = reinterpret_cast<u32x4*>(dst + kvsel * half);
-      for (int64_t i = lane; i < n16; i += 64 * 8) {
-        u32x4 r[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          int64_t idx = i + u * 64;
-          if (idx < n16) r[u] = __builtin_nontemporal_load(s4 + idx);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          int64_t idx = i + u * 64;
-          if (idx < n16) d4[idx] = r[u];
-        }
-      }
-    }
-    if (a.debug_flags & 4) {
-      // Debug: read back what this wave wrote (after its own stores completed).
-      fence_release();
-      uint32_t bad = 0;
-      for (int kvsel = 0; kvsel < 2; ++kvsel) {
-        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + kvsel * half);
-        const u32x4* d4 = reinterpret_cast<const u32x4*>(dst + kvsel * half);
-        for (int64_t i = lane; i < n16; i += 64) {
-          u32x4 x = s4[i], y = d4[i];
-          bad += (x[0] != y[0]) | (x[1] != y[1]) | (x[2] != y[2]) | (x[3] != y[3]);
-        }
-      }
-      if (bad) add32(&a.ctrl->debug_mismatch.v, bad << 16);
-    }
-    dst_off = (int64_t)(dst - a.slots);
-    if (a.stage_delay_ticks > 0) {
-      uint32_t hsh = (k * 2654435761u) ^ (uint32_t)a.epoch;
-      uint64_t until = ticks() + (hsh % (uint32_t)a.stage_delay_ticks);
-      while (ticks() < until) __builtin_amdgcn_s_sleep(1);
-    }
-    fence_release();  // this wave's copies are visible at agent scope
-    if (lane == 0) {
-      uint32_t* cnt = &a.tile_parts[slot * a.n_tiles + j];
-      uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (uint32_t)a.parts_per_tile - 1) {
-        st32(cnt, 0);  // reset for step t + 2 before the flag can release anyone
-        st64_release(&a.slot_flags[slot * a.n_tiles + j], stamp(a.epoch, t));
-      }
-    }
-  }
-  if (lane == 0) {
-    uint64_t busy = ticks() - t_begin - w;
-    add64(&a.ctrl->stage_ticks.v, busy);
-    add32(&a.ctrl->stage_done.v, 1);
-    add64(&a.ctrl->stage_wait_ticks.v, w);
-    if (assist) add32(&a.ctrl->assist_tasks.v, 1);
-    trace_rec(a, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, dst_off);
-  }
-  waited += w;
-  return ok;
+// The compute role's LDS ring holds kStages staged KV blocks. Each stage is its own
+// object so the compiler can tell a block copy into one stage from reads of another
+// (it would otherwise wait for every copy in flight before any LDS read). A staging
+// task borrows the same memory as scratch for its transposes.
+__shared__ __attribute__((aligned(16))) uint8_t g_stage0[Block<128>::kBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage1[Block<128>::kBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage2[Block<128>::kBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage3[Block<128>::kBytes];
+__shared__ int32_t g_cmd[4];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_buf() {
+  static_assert(kStages == 4, "one named buffer per stage");
+  if constexpr (S == 0) return g_stage0;
+  else if constexpr (S == 1) return g_stage1;
+  else if constexpr (S == 2) return g_stage2;
+  else return g_stage3;
 }
 
-// ------------------------------------------------------------------ compute role
-
+// 16-byte chunk positions inside a staged block (see Block<D>).
 template <int D>
-struct Smem {
-  uint16_t k[2][kBN][D + 8];    // K tile rows, bf16 (padded: conflict-free 16-byte reads)
-  uint16_t vt[2][D][kBN + 8];   // V tile transposed to fp16, keys permuted within 16
-  int32_t cmd[4];
-};
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  if constexpr (D == 128) return chunk ^ (row & 15);  // 16 chunks per 256-byte row
+  else return chunk ^ ((row >> 1) & 7);               // 8 chunks per 128-byte row
+}
+__device__ __forceinline__ int swz_v(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Position of key offset x (0..15) inside its group of 16 in the transposed V tile:
-// swaps bits 2 and 3, so each lane's 8 P^T values (keys {0-3,8-11} for lanes 0-31,
-// {4-7,12-15} for lanes 32-63, from the 32x32 accumulator layout) meet the 8
-// contiguous V^T values it reads.
+// Position of key offset x (0..15) inside its group of 16 in a V^T row: swaps bits 2
+// and 3, so each lane's 8 P^T values (keys {0-3,8-11} for lanes 0-31, {4-7,12-15} for
+// lanes 32-63, from the 32x32 accumulator layout) meet 8 contiguous V^T values.
 __device__ __forceinline__ int vt_pos(int key) {
   int x = key & 15;
   return (key & ~15) | (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Exact bf16 -> fp16 for |v| < 65520 (the fp16 range); two values per 32-bit word.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  f16x2 h = {(_Float16)__builtin_bit_cast(float, w << 16), (_Float16)__builtin_bit_cast(float, w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Waits until at most n vector-memory operations of this wave are outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+  // s_waitcnt immediate: vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt
+  // at their maxima (no wait).
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0f76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+  }
+}
+
+// ------------------------------------------------------------------ staging role
+
+// One staging task, run by the whole workgroup: 128-row tile j of the chunk of step
+// t (chunk (rank - t) mod N, read from its home in kv_chunks, which stands for the
+// predecessor's memory) becomes staged blocks in slot t % 2: K swizzled, V transposed
+// to fp16. The slot is free once every unit has finished step t - 2. One release per
+// tile publishes its epoch-stamped flag (paper §4: epoch-stamped readiness flags).
 template <int D>
-__device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, uint64_t& waited) {
+__device__ void stage_tile(const KernelArgs& a, uint32_t k, bool assist) {
+  constexpr int CPR = D / 8;                        // 16-byte chunks per K/V row
+  constexpr int KCH = kBN * CPR / kThreads;         // K (or V) chunks per thread per block
+  constexpr int VPITCH = kBN + 2;                   // fp16 scratch row pitch (breaks bank conflicts)
+  constexpr int NB = 4;                             // blocks per batch (one scratch stage each)
+  static_assert(KCH >= 1 && kBN * CPR % kThreads == 0, "block split");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint64_t t_begin = ticks();
+  const int t = (int)k / a.n_tiles;
+  const int j = (int)k % a.n_tiles;
+  const int slot = t & 1;
+  uint64_t w = 0;
+  // Slot release (every wave waits; a timeout leaves the error word set for all).
+  if (t >= 2) wave_wait_ge32(a, &a.done_count[t - 2], (uint32_t)a.n_units, w);
+  __syncthreads();
+  const bool ok = !has_error(a);
+  __syncthreads();
+  if (ok) {
+    const int c = chunk_of_step(a, t);
+    const int64_t row_elems = (int64_t)a.hkv * D;
+    const uint16_t* kh = a.kv + (int64_t)c * a.chunk_elems;
+    const uint16_t* vh = kh + (int64_t)a.lk * row_elems;
+    uint8_t* sbase = a.slots + (int64_t)slot * a.slot_bytes;
+    const int nb = min(2, a.n_blocks - 2 * j);       // 64-key blocks in this tile
+    const int n_pairs = a.hkv * nb;
+    for (int p0 = 0; p0 < n_pairs; p0 += NB) {
+      u32x4 kr[NB][KCH], vr[NB][KCH];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int p = p0 + b;
+        const int g = p / nb, kb = 2 * j + p % nb;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+          const int q = tid + i * kThreads, r = q / CPR, cc = q % CPR, key = kb * kBN + r;
+          const bool in = p < n_pairs && key < a.lk;
+          const int64_t off = ((int64_t)key * a.hkv + g) * D + 8 * cc;
+          kr[b][i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + off)) : u32x4{0, 0, 0, 0};
+          vr[b][i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + off)) : u32x4{0, 0, 0, 0};
+        }
+      }
+      uint8_t* scr[NB] = {g_stage0, g_stage1, g_stage2, g_stage3};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int p = p0 + b;
+        if (p >= n_pairs) break;
+        const int g = p / nb, kb = 2 * j + p % nb;
+        uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+          const int q = tid + i * kThreads, r = q / CPR, cc = q % CPR;
+          *reinterpret_cast<u32x4*>(blk + r * (D * 2) + 16 * swz_k<D>(r, cc)) = kr[b][i];
+          // V: 8 consecutive d of key r -> fp16 column vt_pos(r) of 8 scratch rows.
+          uint16_t* sc = reinterpret_cast<uint16_t*>(scr[b]);
+          const int pos = vt_pos(r);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h2 = bf16x2_to_f16x2(vr[b][i][e]);
+            sc[(8 * cc + 2 * e) * VPITCH + pos] = (uint16_t)(h2 & 0xffffu);
+            sc[(8 * cc + 2 * e + 1) * VPITCH + pos] = (uint16_t)(h2 >> 16);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int p = p0 + b;
+        if (p >= n_pairs) break;
+        const int g = p / nb, kb = 2 * j + p % nb;
+        uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes + Block<D>::kKBytes;
+        const uint16_t* sc = reinterpret_cast<const uint16_t*>(scr[b]);
+        for (int q = tid; q < D * 8; q += kThreads) {
+          const int d = q / 8, cc = q % 8;
+          const uint16_t* row = sc + d * VPITCH + 8 * cc;  // 4-byte aligned (VPITCH even)
+          u32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const uint32_t*>(row + 2 * e);
+          *reinterpret_cast<u32x4*>(blk + d * 128 + 16 * swz_v(d, cc)) = v;
+        }
+      }
+      __syncthreads();
+    }
+    if (a.debug_flags & 1) {
+      // Debug: re-derive the K part of every block of the tile from the chunk's home.
+      uint32_t bad = 0;
+      for (int p = 0; p < n_pairs; ++p) {
+        const int g = p / nb, kb = 2 * j + p % nb;
+        const uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes;
+        for (int q = tid; q < kBN * CPR; q += kThreads) {
+          const int r = q / CPR, cc = q % CPR, key = kb * kBN + r;
+          u32x4 want = key < a.lk ? *reinterpret_cast<const u32x4*>(kh + ((int64_t)key * a.hkv + g) * D + 8 * cc)
+                                  : u32x4{0, 0, 0, 0};
+          u32x4 got = *reinterpret_cast<const u32x4*>(blk + r * (D * 2) + 16 * swz_k<D>(r, cc));
+          bad += (want[0] != got[0]) | (want[1] != got[1]) | (want[2] != got[2]) | (want[3] != got[3]);
+        }
+      }
+      if (bad) add32(&a.ctrl->debug_mismatch.v, bad);
+      __syncthreads();
+    }
+    if (a.stage_delay_ticks > 0 && tid == 0) {
+      uint32_t hsh = (k * 2654435761u) ^ (uint32_t)a.epoch;
+      uint64_t until = ticks() + (hsh % (uint32_t)a.stage_delay_ticks);
+      while (ticks() < until) __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  // Every wave's stores precede the barrier; one agent-scope release by thread 0
+  // then covers the whole tile (workgroup-scope order, then agent scope).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0) {
+    if (ok) st64_release(&a.slot_flags[slot * a.n_tiles + j], stamp(a.epoch, t));
+    const uint64_t busy = ticks() - t_begin - w;
+    add64(&a.ctrl->stage_ticks.v, busy);
+    add32(&a.ctrl->stage_done.v, 1);
+    add64(&a.ctrl->stage_wait_ticks.v, w);
+    if (assist) add32(&a.ctrl->assist_tasks.v, 1);
+    trace_rec(kernel_args(), kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
+  }
+  (void)lane;
+}
+
+// ------------------------------------------------------------------ compute role
+
+// Copies staged block `src` (global) into LDS stage S: each wave moves 1 KB per
+// instruction with global_load_lds_dwordx4 (no registers, no VALU).
+template <int D, int S>
+__device__ __forceinline__ void dma_block(const uint8_t* src) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < Block<D>::kChunksPerThread; ++i) {
+    const int ch = i * kThreads + w * 64;
+    __builtin_amdgcn_global_load_lds(src + (int64_t)(ch + lane) * 16, (lds_void*)(stage_buf<S>() + ch * 16), 16, 0, 0);
+  }
+}
+
+template <int D>
+__device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& waited) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
-  constexpr int KCH = kBN * D / 8 / kThreads;   // 16-byte K chunks per thread per tile
-  constexpr int NVG = (kBN / 4) * (D / 4);      // V groups (4 keys x 4 d) per tile
-  constexpr int VSTRIDE = kBN + 8;
-  static_assert(KCH >= 1 && NVG <= kThreads, "tile split");
+  constexpr int NI = Block<D>::kChunksPerThread;  // block-copy instructions per wave per tile
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
@@ -338,9 +435,7 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
   const bool wave_rows = q0w < a.lq;
   const int qrow = q0w + col;
   const bool diag = a.causal && t == 0;
-  const int c = chunk_of_step(a, t);
-  const uint16_t* kbase = (t == 0) ? a.kv + (int64_t)c * a.chunk_elems : a.slots + (int64_t)(t & 1) * a.chunk_elems;
-  const int64_t half = (int64_t)a.lk * a.hkv * D;
+  const uint8_t* sblk = a.slots + (int64_t)(t & 1) * a.slot_bytes + (int64_t)kvh * a.n_blocks * Block<D>::kBytes;
   const int q_end = min(a.lq, qb * a.bq + a.bq);
   const int kend = diag ? min(a.lk, q_end) : a.lk;
   const int n_kt = (kend + kBN - 1) / kBN;
@@ -357,7 +452,7 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
   const uint64_t st = stamp(a.epoch, t);
   const int n_st = (kend + kStageRows - 1) / kStageRows;
   int ready_upto = n_st;
-  if (t > 0) {
+  {
     bool mine = true;
     for (int j = lane; j < n_st; j += 64) mine &= (ld64(&flags[j]) == st);
     if (__all(mine)) {
@@ -379,7 +474,9 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
     }
   }
 
-  // Running state: O^T blocks, max (log2 units of the scaled score), partial sum.
+  // Running state: O^T blocks, max (log2 units of the scaled score), and two running
+  // sums: l of the exact P (for the log-sum-exp) and lr of the fp16-rounded P that the
+  // PV product weights V with (for the normalisation, see below).
   f32x16 o[DB];
   float m_run, l_run, lr_run;
   float* accw = a.acc + ((int64_t)unit * kWaves + w) * (32 * D + 256);
@@ -404,192 +501,128 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
     lr_run = ml[2];
   }
 
-  // Tile loads: K as 16-byte row chunks; V as 4 keys x 8 d per thread, transposed on
-  // the way into LDS.
-  u32x4 kreg[KCH];
-  u32x2 vreg[4];
-  auto wait_tile = [&](int kt) {
-    int j = (kt * kBN) / kStageRows;
+  // Per-lane LDS offsets (the swizzles depend only on the lane).
+  const int k_off = col * (D * 2);                // + kb*32*(D*2) + 16*swz
+  const int kx = (D == 128) ? (col & 15) : ((col >> 1) & 7);
+  const int v_off = Block<D>::kKBytes + col * 128;  // + db*32*128 + 16*swz
+  const int vx = (col >> 1) & 7;
+
+  auto issue = [&](int kt, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int j = (kt * kBN) / kStageRows;
     if (j >= ready_upto) {
       ok &= wave_wait_stamp(a, &flags[j], st, waited);
       ready_upto = j + 1;
     }
+    dma_block<D, S>(sblk + (int64_t)kt * Block<D>::kBytes);
   };
-  auto load_tile = [&](int kt) {
+
+  auto compute_tile = [&](int kt, const uint8_t* sb) {
+    // S^T = K Q^T for 2 blocks of 32 keys.
+    f32x16 s[kBN / 32];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      s[kb] = f32x16{};
+      const uint8_t* kr = sb + kb * 32 * (D * 2) + k_off;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * kk + hi) ^ kx));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[kk], s[kb], 0, 0, 0);
+      }
+    }
+    // Masks: ragged key tail, and keys after the query on the diagonal step.
     const int k0 = kt * kBN;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int ch = tid + i * kThreads;
-      int key = k0 + ch / (D / 8);
-      int dd = (ch % (D / 8)) * 8;
-      kreg[i] = key < a.lk ? *reinterpret_cast<const u32x4*>(kbase + ((int64_t)key * a.hkv + kvh) * D + dd)
-                           : u32x4{0, 0, 0, 0};
-    }
-    if (tid < NVG) {
-      int key4 = k0 + (tid / (D / 4)) * 4;
-      int dd = (tid % (D / 4)) * 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int key = key4 + r;
-        vreg[r] = key < a.lk
-                      ? *reinterpret_cast<const u32x2*>(kbase + half + ((int64_t)key * a.hkv + kvh) * D + dd)
-                      : u32x2{0, 0};
-      }
-    }
-    if ((a.debug_flags & 1) && t > 0) {
-      // Debug: compare what was read from the slot with the chunk's home copy.
-      const uint16_t* home = a.kv + (int64_t)c * a.chunk_elems;
-      uint32_t bad = 0;
-      for (int i = 0; i < KCH; ++i) {
-        int ch = tid + i * kThreads;
-        int key = k0 + ch / (D / 8);
-        int dd = (ch % (D / 8)) * 8;
-        if (key < a.lk) {
-          u32x4 r = *reinterpret_cast<const u32x4*>(home + ((int64_t)key * a.hkv + kvh) * D + dd);
-          bad += (r[0] != kreg[i][0]) | (r[1] != kreg[i][1]) | (r[2] != kreg[i][2]) | (r[3] != kreg[i][3]);
-        }
-      }
-      if (tid < NVG) {
-        int key4 = k0 + (tid / (D / 4)) * 4;
-        int dd = (tid % (D / 4)) * 4;
-        for (int r = 0; r < 4; ++r) {
-          int key = key4 + r;
-          if (key < a.lk) {
-            u32x2 v = *reinterpret_cast<const u32x2*>(home + half + ((int64_t)key * a.hkv + kvh) * D + dd);
-            bad += (v[0] != vreg[r][0]) | (v[1] != vreg[r][1]);
-          }
-        }
-      }
-      if (bad) add32(&a.ctrl->debug_mismatch.v, bad);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int ch = tid + i * kThreads;
-      int key = ch / (D / 8);
-      int dd = (ch % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][key][dd]) = kreg[i];
-    }
-    if (tid < NVG) {
-      // vreg[r] holds d = dd..dd+3 of key key4+r as bf16 pairs. Each of the 4 d rows
-      // of V^T gets the 4 keys, converted to fp16 (exact for |v| < 65520).
-      int key4 = (tid / (D / 4)) * 4;
-      int dd = (tid % (D / 4)) * 4;
-      int pos = vt_pos(key4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float f[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t wv = vreg[r][e >> 1];
-          f[r] = __builtin_bit_cast(float, (e & 1) ? (wv & 0xffff0000u) : (wv << 16));
-        }
-        f16x2 p01 = {(_Float16)f[0], (_Float16)f[1]};
-        f16x2 p23 = {(_Float16)f[2], (_Float16)f[3]};
-        *reinterpret_cast<u32x2*>(&sm.vt[buf][dd + e][pos]) =
-            u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-      }
-    }
-  };
-
-  if (n_kt > 0) {
-    if (t > 0) wait_tile(0);
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) {
-      if (t > 0) wait_tile(kt + 1);
-      load_tile(kt + 1);
-    }
-    if (kt < w_kt) {
-      const uint16_t* ks = &sm.k[buf][0][0];
-      const uint16_t* vs = &sm.vt[buf][0][0];
-      // S^T = K Q^T for 2 blocks of 32 keys.
-      f32x16 s[kBN / 32];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* kr = ks + (kb * 32 + col) * (D + 8) + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[kk], s[kb], 0, 0, 0);
-        }
-      }
-      // Masks: ragged key tail, and keys after the query on the diagonal step.
-      const int k0 = kt * kBN;
-      if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            int key = k0 + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key >= a.lk || (diag && key > qrow)) s[kb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = mx * c2;
-      // Online-softmax update (FlashAttention-2), rescaling only when the max has
-      // grown by more than kTau since the last rescale.
-      if (__any(mxs > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mxs);
-        const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        l_run *= alpha;
-        lr_run *= alpha;
-        m_run = m_new;
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      f16x8 pb[kBN / 16];
-      float lsum = 0.f;
+    if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-          lsum += pv;
-          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
+          int key = k0 + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          if (key >= a.lk || (diag && key > qrow)) s[kb][i] = -INFINITY;
         }
-      l_run += lsum;
-      // Two running sums: l (exact P, for the log-sum-exp) and lr, the sum of the
-      // fp16-rounded P that the PV product actually weights V with (two per
-      // v_dot2c_f32_f16 against (1, 1)). Normalising O by lr makes the applied
-      // weights sum to one, so a dominant key's rounding cancels in O / lr.
-      float ls0 = 0.f, ls1 = 0.f;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * c2;
+    // Online-softmax update (FlashAttention-2), rescaling only when the max has grown
+    // by more than kTau since the last rescale.
+    if (__any(mxs > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      l_run *= alpha;
+      lr_run *= alpha;
+      m_run = m_new;
+    }
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    f16x8 pb[kBN / 16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
+        lsum += pv;
+        pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
+      }
+    l_run += lsum;
+    // lr sums the fp16-rounded P (two per v_dot2c_f32_f16 against (1, 1)); normalising
+    // O by it makes the applied weights sum to one, so a dominant key's rounding
+    // cancels in O / lr.
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < kBN / 16; ++pp) {
+      ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 0, 1), kOnes2, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 2, 3), kOnes2, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 4, 5), kOnes2, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 6, 7), kOnes2, ls1, false);
+    }
+    lr_run += ls0 + ls1;
+    // O^T += V^T P^T (fp16 operands, fp32 accumulation).
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint8_t* vr = sb + db * 32 * 128 + v_off;
 #pragma unroll
       for (int pp = 0; pp < kBN / 16; ++pp) {
-        ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 0, 1), kOnes2, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 2, 3), kOnes2, ls1, false);
-        ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 4, 5), kOnes2, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 6, 7), kOnes2, ls1, false);
-      }
-      lr_run += ls0 + ls1;
-      // O^T += V^T P^T (fp16 operands, fp32 accumulation).
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vr = vs + (db * 32 + col) * VSTRIDE + hi * 8;
-#pragma unroll
-        for (int pp = 0; pp < kBN / 16; ++pp) {
-          f16x8 av = *reinterpret_cast<const f16x8*>(vr + pp * 16);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[pp], o[db], 0, 0, 0);
-        }
+        f16x8 av = *reinterpret_cast<const f16x8*>(vr + 16 * ((2 * pp + hi) ^ vx));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[pp], o[db], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  auto step = [&](int kt, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (kt >= n_kt) return;
+    // This wave's copies of tile kt are done once at most the newer tiles' copies
+    // remain; the barrier makes every wave's part visible and frees stage S-1.
+    const int newer = min(kStages - 2, n_kt - 1 - kt);
+    wait_vm(newer * NI);
+    __builtin_amdgcn_s_barrier();
+    // Refill stage S-1 (freed by the barrier) with tile kt+3: now if its staged tile
+    // is known to be ready, else after this tile's compute (the wait may block).
+    const int kn = kt + kStages - 1;
+    const bool early = kn < n_kt && (kn * kBN) / kStageRows < ready_upto;
+    if (early) issue(kn, std::integral_constant<int, (S + kStages - 1) % kStages>{});
+    if (kt < w_kt) compute_tile(kt, stage_buf<S>());
+    if (kn < n_kt && !early) issue(kn, std::integral_constant<int, (S + kStages - 1) % kStages>{});
+  };
+
+  // Prologue: kStages-1 blocks in flight, then one per tile.
+  if (0 < n_kt) issue(0, std::integral_constant<int, 0>{});
+  if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
+  if (2 < n_kt) issue(2, std::integral_constant<int, 2>{});
+  for (int kt = 0; kt < n_kt; kt += kStages) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
+    step(kt + 3, std::integral_constant<int, 3>{});
   }
 
   if (ok && wave_rows) {
@@ -624,8 +657,9 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
       reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, lr_run, 0.f};
     }
   }
-  // Publish: unit step done (orders the state for step t+1) and slot release.
-  fence_release();
+  // Publish: unit step done (orders the state for step t+1) and slot release. Every
+  // wave's stores precede the barrier; one agent-scope release by thread 0 covers them.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0 && !has_error(a)) {
     st64_release(&a.unit_flags[unit], stamp(a.epoch, t));
@@ -639,12 +673,8 @@ __device__ void compute_task(const KernelArgs& a, Smem<D>& sm, int unit, int t, 
 // released (every unit has finished step - 2), so running it waits for nothing.
 __device__ __forceinline__ bool stage_claimable(const KernelArgs& a, uint32_t h, int bound) {
   if ((int)h >= a.n_stage_tasks) return false;
-  const int step = 1 + (int)h / (a.n_tiles * a.parts_per_tile);
+  const int step = (int)h / a.n_tiles;
   return step <= bound && (step < 2 || ld32(&a.done_count[step - 2]) >= (uint32_t)a.n_units);
-}
-
-__device__ __forceinline__ bool assist_claimable(const KernelArgs& a, int bound) {
-  return stage_claimable(a, ld32(&a.ctrl->stage_head.v), bound);
 }
 
 // Claim the next compute task. Each XCD has a queue of the units of its head groups,
@@ -653,7 +683,8 @@ __device__ __forceinline__ bool assist_claimable(const KernelArgs& a, int bound)
 // queue, else from the slowest queue: every claimed task then needs only staging of
 // steps whose slot release depends on tasks already claimed, so the schedule cannot
 // deadlock whatever subset of workgroups is resident. Run by one lane.
-__device__ __noinline__ bool claim_compute(const KernelArgs& a, int& unit, int& step) {
+__device__ __noinline__ bool claim_compute(const KernelArgs* ap, int& unit, int& step) {
+  const KernelArgs& a = *ap;
   const int own = (int)(blockIdx.x % (unsigned)a.n_xcd);
   for (int attempt = 0; attempt < 1 << 20; ++attempt) {
     if (has_error(a)) return false;
@@ -682,8 +713,7 @@ __device__ __noinline__ bool claim_compute(const KernelArgs& a, int& unit, int& 
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
-  __shared__ Smem<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const uint64_t t_start = ticks();
   uint32_t role = ((int)blockIdx.x < a.initial_stagers) ? kRoleStage : kRoleCompute;
   if (tid == 0) {
@@ -693,8 +723,6 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       max32(&a.ctrl->max_stage.v, n);
     }
   }
-  uint64_t waited = 0;
-  bool fresh_stager = (role == kRoleStage);
   // A claimed compute task not yet run (thread 0 only).
   bool pending = false;
   int32_t pend_u = 0, pend_t = 0;
@@ -702,121 +730,95 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   while (true) {
     __syncthreads();
     if (tid == 0) {
-      int32_t op = kOpExit, u = 0, s = 0;
+      int32_t op = kOpExit, x = 0, y = 0;
       if (!has_error(a)) {
-        maybe_controller(a);
+        maybe_controller(kernel_args());
         const bool stage_left = (int)ld32(&a.ctrl->stage_head.v) < a.n_stage_tasks;
         if (!pending) {
-          if (role == kRoleStage && !fresh_stager) {
-            // Back from a staging round: leave the role when staging is done or the
-            // target has dropped below the current count.
+          // Role changes happen at task boundaries (§3.2): leave the staging role when
+          // staging is done or the target dropped below the count; join it when the
+          // count is below the target.
+          if (role == kRoleStage) {
             uint32_t ns = ld32(&a.ctrl->n_stage.v);
-            if (!stage_left ||
-                (!a.split_fixed && (int)ns > current_target(a) && cas32(&a.ctrl->n_stage.v, ns, ns - 1))) {
-              if (!stage_left) add32(&a.ctrl->n_stage.v, (uint32_t)-1);
+            if (!stage_left) {
+              add32(&a.ctrl->n_stage.v, (uint32_t)-1);
+              role = kRoleCompute;
+            } else if (!a.split_fixed && (int)ns > current_target(a) && cas32(&a.ctrl->n_stage.v, ns, ns - 1)) {
               role = kRoleCompute;
               add32(&a.ctrl->role_switches.v, 1);
-              trace_rec(a, kTraceRole, 0, ld32(&a.ctrl->n_stage.v), 0, 0, 0, 0);
+              trace_rec(kernel_args(), kTraceRole, 0, ns - 1, 0, 0, 0, 0);
             }
-          }
-          fresh_stager = false;
-          if (role == kRoleCompute && !a.split_fixed && !a.disable_staging && stage_left) {
+          } else if (!a.split_fixed && !a.disable_staging && stage_left) {
             uint32_t ns = ld32(&a.ctrl->n_stage.v);
             if ((int)ns < current_target(a) && cas32(&a.ctrl->n_stage.v, ns, ns + 1)) {
               role = kRoleStage;
               max32(&a.ctrl->max_stage.v, ns + 1);
               add32(&a.ctrl->role_switches.v, 1);
-              trace_rec(a, kTraceRole, 1, ns + 1, 0, 0, 0, 0);
+              trace_rec(kernel_args(), kTraceRole, 1, ns + 1, 0, 0, 0, 0);
             }
           }
           if (role == kRoleStage) {
-            op = kOpStage;
-          } else if (claim_compute(a, pend_u, pend_t)) {
-            pending = true;
-          } else if (stage_left && !a.disable_staging) {
-            // No compute task left to claim: drain the remaining staging, whatever
-            // the target (u = 1 tells the waves to ignore it).
-            role = kRoleStage;
-            uint32_t n = add32(&a.ctrl->n_stage.v, 1) + 1;
-            max32(&a.ctrl->max_stage.v, n);
-            op = kOpStage;
-            u = 1;
+            uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
+            if ((int)kk < a.n_stage_tasks) {
+              op = kOpStage;
+              x = (int32_t)kk;
+            } else {
+              add32(&a.ctrl->n_stage.v, (uint32_t)-1);
+              role = kRoleCompute;
+            }
+          }
+          if (op == kOpExit && role == kRoleCompute) {
+            if (claim_compute(kernel_args(), pend_u, pend_t)) {
+              pending = true;
+            } else if (stage_left && !a.disable_staging) {
+              // No compute task left to claim: help drain the remaining staging.
+              uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
+              if ((int)kk < a.n_stage_tasks) {
+                op = kOpStage;
+                x = (int32_t)kk;
+              }
+            }
           }
         }
         if (pending) {
-          // Stall rule of §3.2: while staging work that its task depends on is still
+          // Stall rule of §3.2: while staging work that the claimed task depends on is
           // unclaimed (tasks of steps up to its own whose slot is already released),
-          // a compute workgroup does that work first; once every such task is
+          // the compute workgroup does that work first; once every such task is
           // claimed, the data its task waits for is in the hands of running waves.
-          if (pend_t > 0 && !a.disable_staging && assist_claimable(a, pend_t)) {
-            op = kOpAssist;
-            s = pend_t;
+          uint32_t h = ld32(&a.ctrl->stage_head.v);
+          if (!a.disable_staging && stage_claimable(a, h, pend_t) && cas32(&a.ctrl->stage_head.v, h, h + 1)) {
+            op = kOpStage;
+            x = (int32_t)h;
+            y = 1;
           } else {
             op = kOpCompute;
-            u = pend_u;
-            s = pend_t;
+            x = pend_u;
+            y = pend_t;
             pending = false;
           }
         }
       }
-      sm.cmd[0] = op;
-      sm.cmd[1] = u;
-      sm.cmd[2] = s;
+      g_cmd[0] = op;
+      g_cmd[1] = x;
+      g_cmd[2] = y;
     }
     __syncthreads();
-    const int op = sm.cmd[0];
+    const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
     if (op == kOpExit) break;
     if (op == kOpCompute) {
-      const int cu = sm.cmd[1], ct = sm.cmd[2];
       const uint64_t t0 = ticks();
       uint64_t w0 = 0;
-      compute_task<D>(a, sm, cu, ct, w0);
+      compute_task<D>(a, x, y, w0);
       if (tid == 0) {
         const uint64_t busy = ticks() - t0 - w0;
         add64(&a.ctrl->compute_ticks.v, busy);
         add32(&a.ctrl->compute_done.v, 1);
         add64(&a.ctrl->compute_wait_ticks.v, w0);
-        trace_rec(a, kTraceCompute, cu, ct, (int64_t)t0, (int64_t)w0, 0, 0);
-      }
-      waited += w0;
-    } else if (op == kOpAssist) {
-      // One staging task per wave, claimed only if its slot is already free.
-      const int bound = sm.cmd[2];
-      uint32_t k = 0xffffffffu;
-      if (lane == 0) {
-        for (int attempt = 0; attempt < 8 && k == 0xffffffffu; ++attempt) {
-          uint32_t h = ld32(&a.ctrl->stage_head.v);
-          if (!stage_claimable(a, h, bound)) break;
-          if (cas32(&a.ctrl->stage_head.v, h, h + 1)) k = h;
-        }
-      }
-      k = wave_bcast(k);
-      if (k != 0xffffffffu) {
-        uint64_t w1 = 0;
-        stage_task(a, k, true, w1);
+        trace_rec(kernel_args(), kTraceCompute, x, y, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
-      // Staging round: every wave claims and runs staging tasks on its own until
-      // staging runs out or the controller lowers the target below the count.
-      const bool drain = sm.cmd[1] != 0;
-      while (true) {
-        uint32_t k = 0xffffffffu;
-        if (lane == 0) {
-          if (!has_error(a)) {
-            bool stop = !drain && !a.split_fixed && (int)ld32(&a.ctrl->n_stage.v) > current_target(a);
-            if (!stop) {
-              uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
-              if ((int)kk < a.n_stage_tasks) k = kk;
-            }
-          }
-        }
-        k = wave_bcast(k);
-        if (k == 0xffffffffu) break;
-        uint64_t w1 = 0;
-        stage_task(a, k, false, w1);
-        if (lane == 0) maybe_controller(a);
-        if (a.debug_flags & 2) break;
-      }
+      stage_tile<D>(a, (uint32_t)x, y != 0);
+      if (tid == 0) maybe_controller(kernel_args());
     }
   }
 
@@ -853,15 +855,11 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
     ds->kernel_ticks = (int64_t)(ld64(&cb->t_last.v) - ~ld64(&cb->t_first.v));
     ds->trace_records = (int64_t)ld32(&cb->trace_head.v);
     ds->debug_mismatch = (int64_t)ld32(&cb->debug_mismatch.v);
-    sm.cmd[3] = (int32_t)err;
   }
   __syncthreads();
-  const bool had_error = sm.cmd[3] != 0;
   uint32_t* words = reinterpret_cast<uint32_t*>(cb);
   for (int i = tid; i < (int)(sizeof(DevCtrl) / 4); i += kThreads) words[i] = 0;
   for (int i = tid; i < a.n_steps; i += kThreads) a.done_count[i] = 0;
-  if (had_error)
-    for (int i = tid; i < 2 * a.n_tiles; i += kThreads) a.tile_parts[i] = 0;
 }
 
 template __global__ void ring_attn_kernel<64>(KernelArgs);

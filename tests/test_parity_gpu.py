@@ -102,7 +102,7 @@ def test_full_size_workloads_sampled(idx):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     assert stats["status"] == 0
     assert stats["compute_tasks_done"] == stats["n_units"] * stats["n_steps"]
-    assert stats["staging_tasks_done"] == stats["n_stage_parts"]
+    assert stats["staging_tasks_done"] == stats["n_stage_tasks"]
 
 
 SPLIT_VARIANTS = [
@@ -114,7 +114,7 @@ SPLIT_VARIANTS = [
     dict(grid_wgs=1),
     dict(grid_wgs=2),
     dict(grid_wgs=8),
-    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, debug_flags=7),
+    dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, debug_flags=1),
 ]
 
 
@@ -250,7 +250,7 @@ def test_stats_and_controller_follow_eq2():
     print("    stats:", st, flush=True)
     assert st["status"] == 0
     assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]
-    assert st["staging_tasks_done"] == st["n_stage_parts"]
+    assert st["staging_tasks_done"] == st["n_stage_tasks"]
     recs = mk.mk_ring_attn_trace()
     ctrl = [r for r in recs if r[2] == 3]
     comp = [r for r in recs if r[2] == 1]
