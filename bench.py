@@ -1,7 +1,8 @@
 """Benchmark of the per-rank ring-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--sweep] [--verify]
+                    [--sweep] [--verify] [--copy-calibration-mib M]
+    python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
 
 A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
 rank, staging included) over one batch of synthetic input already resident in HBM.
@@ -71,6 +72,50 @@ def stored_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(run_dir):
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    return rows
+
+
+def write_traffic(cfg, pmc_dir, copy_mib):
+    """HBM bytes per launch of the ring kernel from two rocprofv3 --pmc runs of
+    `bench.py --copy-calibration-mib M` (FETCH_SIZE under pmc_dir/fetch, WRITE_SIZE
+    under pmc_dir/write). Each counter is scaled by what it reads for the plain
+    device copy of M MiB in the same run (largest copyBuffer dispatches)."""
+    res = {}
+    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(os.path.join(pmc_dir, sub)) if r["Counter_Name"] == counter]
+        ring = [float(r["Counter_Value"]) for r in rows if "ring_attn_kernel" in r["Kernel_Name"]]
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not ring or not copies:
+            raise SystemExit(f"{counter}: missing ring kernel or copy dispatches in {pmc_dir}/{sub}")
+        gmax = max(int(r["Grid_Size"]) for r in copies)
+        cal = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == gmax]
+        copy_kib = sum(cal) / len(cal)
+        moved = copy_mib * 1024.0  # KiB read (FETCH) or written (WRITE) by the copy
+        scale = moved / copy_kib
+        kib = sum(ring) / len(ring)
+        res[counter] = {"kib_per_dispatch": kib, "dispatches": len(ring), "copy_kib_per_dispatch": copy_kib,
+                        "copy_dispatches": len(cal), "scale": scale, "bytes_per_launch": kib * 1024.0 * scale}
+    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    out = {"workload": cfg.name, "kernel": "mkra::ring_attn_kernel<%d>" % cfg.d, "kernel_sha": kernel_hash(),
+           "copy_calibration_mib": copy_mib, "counters": res, "hbm_bytes_per_launch": int(total),
+           "algorithmic_bytes": algorithmic_bytes(cfg)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    log(f"[bench] wrote {path}: {total / 1e6:.1f} MB per launch "
+        f"(FETCH x{res['FETCH_SIZE']['scale']:.3f}, WRITE x{res['WRITE_SIZE']['scale']:.3f})")
+
+
 def cpu_baseline(cfg, q, kv, budget_rows):
     """The fp64 oracle on the host cores, on a bounded sample of the same workload:
     `budget_rows` query rows spread over the chunk, all heads, all keys."""
@@ -121,10 +166,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="name of a workload in ring_inputs.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--sweep", action="store_true", help="also time fixed staging splits vs adaptive (stderr)")
     ap.add_argument("--verify", action="store_true", help="check sampled rows against the oracle (stderr)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 times), the known-size "
+                         "reference that scales the HBM byte counters")
+    ap.add_argument("--traffic-from", default=None,
+                    help="no GPU: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs (DIR/fetch, DIR/write) into "
+                         "profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        from ring_inputs import CONFIGS, CONFIG_BY_NAME
+
+        cfg = CONFIG_BY_NAME[args.workload] if args.workload else CONFIGS[2]
+        write_traffic(cfg, args.traffic_from, args.copy_calibration_mib or 1024)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
@@ -161,6 +218,14 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / k  # ms per launch
 
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration_mib} MiB")
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
