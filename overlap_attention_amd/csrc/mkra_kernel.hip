@@ -20,8 +20,13 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mkra_args.h"
+
+#ifndef MKRA_LDS_AHEAD
+#define MKRA_LDS_AHEAD 6
+#endif
 
 namespace mkra {
 
@@ -35,11 +40,10 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-// Lazy rescale threshold (log2 units): the running max used for exponentials may lag
-// the true max by up to this much; P stays <= 2^kTau, exact algebra is unchanged.
-constexpr float kTau = 8.0f;
+// Lazy rescale bound: while each lane's partial sum of a block's P stays at or below
+// kSumMax, the running max used for the exponentials is kept (see compute_task).
+constexpr float kSumMax = 16384.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
 
 enum : int32_t { kOpExit = 0, kOpCompute = 1, kOpStage = 2 };
 
@@ -51,6 +55,8 @@ __device__ __forceinline__ uint64_t ticks() { return __builtin_amdgcn_s_memrealt
 // the by-value KernelArgs parameter is the first argument). Out-of-line functions
 // read them through this pointer, so the by-value parameter is never address-taken
 // and never copied to scratch memory.
+// Valid only in the kernel's own body (in a called function the intrinsic has no
+// segment to return): out-of-line functions receive the pointer as an argument.
 __device__ __forceinline__ const KernelArgs* kernel_args() {
   return (const KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
 }
@@ -97,6 +103,13 @@ __device__ __forceinline__ uint64_t stamp(uint64_t epoch, int step) {
 
 __device__ __forceinline__ uint32_t wave_bcast(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// max(a, b, c) in one v_max3_f32 (the library fmaxf would first quiet NaN inputs).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ bool has_error(const KernelArgs& a) { return ld32(&a.ctrl->error.v) != kErrNone; }
 
 __device__ __forceinline__ void raise_error(const KernelArgs& a, uint32_t code) {
@@ -109,7 +122,7 @@ __device__ __forceinline__ int chunk_of_step(const KernelArgs& a, int t) {
 }
 
 __device__ __noinline__ void trace_rec(const KernelArgs* ap, int kind, int64_t v0, int64_t v1, int64_t v2, int64_t v3,
-                          int64_t v4, int64_t v5) {
+                                       int64_t v4, int64_t v5) {
   const KernelArgs& a = *ap;
   if (a.trace == nullptr) return;
   uint32_t i = add32(&a.ctrl->trace_head.v, 1);
@@ -137,36 +150,35 @@ __device__ __forceinline__ int eq2_target(int64_t b, int64_t rp, int64_t rs, int
   return (int)(n < lo ? lo : (n > hi ? hi : n));
 }
 
-__device__ __forceinline__ int current_target(const KernelArgs& a) {
-  uint32_t v = ld32(&a.ctrl->target.v);  // 0 = not yet set by the controller
-  return v == 0 ? a.initial_stagers : (int)v - 1;
+template <class KA>
+__device__ __forceinline__ int target_of(const KA& a, uint32_t v) {
+  return v == 0 ? a.initial_stagers : (int)v - 1;  // 0 = not yet set by the controller
 }
+__device__ __forceinline__ int current_target(const KernelArgs& a) { return target_of(a, ld32(&a.ctrl->target.v)); }
 
-__device__ __forceinline__ int64_t units_in_queue(const KernelArgs& a, int x) {
+template <class KA>
+__device__ __forceinline__ int64_t units_in_queue(const KA& a, int x) {
   return a.xcd_unit_begin[x + 1] - a.xcd_unit_begin[x];
 }
 
-__device__ int64_t compute_claimed(const KernelArgs& a) {
-  int64_t s = 0;
-  for (int x = 0; x < a.n_xcd; ++x) {
-    int64_t tot = units_in_queue(a, x) * a.n_steps;
-    int64_t h = ld32(&a.ctrl->xcd_head[x].v);
-    s += h < tot ? h : tot;
-  }
-  return s;
-}
-
-// Run by one lane. Rate-limited by a compare-and-swap on the update time.
-__device__ __noinline__ void maybe_controller(const KernelArgs* ap) {
+// Run by one lane, from a snapshot of the queue heads and the staging head.
+// Rate-limited by a compare-and-swap on the update time.
+__device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uint32_t (&heads)[kMaxXcd],
+                                                 uint32_t stage_head, uint64_t last) {
   const KernelArgs& a = *ap;
   if (a.split_fixed || a.disable_staging) return;
   uint64_t now = ticks();
-  uint64_t last = ld64(&a.ctrl->ctrl_time.v);
   if (last != 0 && now - last < a.ctrl_period_ticks) return;
   if (!cas64(&a.ctrl->ctrl_time.v, last, now)) return;
-  int64_t sh = ld32(&a.ctrl->stage_head.v);
-  int64_t rs = a.n_stage_tasks - (sh < a.n_stage_tasks ? sh : a.n_stage_tasks);
-  int64_t rp = (int64_t)a.n_units * a.n_steps - compute_claimed(a);
+  int64_t rs = a.n_stage_tasks - ((int)stage_head < a.n_stage_tasks ? (int)stage_head : a.n_stage_tasks);
+  int64_t claimed = 0;
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x) {
+    if (x >= a.n_xcd) break;
+    int64_t tot = units_in_queue(a, x) * a.n_steps;
+    claimed += (int64_t)heads[x] < tot ? (int64_t)heads[x] : tot;
+  }
+  int64_t rp = (int64_t)a.n_units * a.n_steps - claimed;
   uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
   uint64_t sd = ld32(&a.ctrl->stage_done.v), stt = ld64(&a.ctrl->stage_ticks.v);
   int64_t cp = cd ? (int64_t)(ct / cd) : a.cost_compute0;
@@ -178,7 +190,6 @@ __device__ __noinline__ void maybe_controller(const KernelArgs* ap) {
   add32(&a.ctrl->ctrl_updates.v, 1);
   trace_rec(ap, kTraceController, rp, rs, cp, cs, a.grid, n);
 }
-
 // ------------------------------------------------------------------ waits
 // All waits are bounded: past timeout_ticks they raise MK_E_TIMEOUT, and every wait
 // returns early once any error is raised, so every workgroup reaches its exit.
@@ -224,23 +235,48 @@ __device__ bool wave_wait_stamp(const KernelArgs& a, const uint64_t* p, uint64_t
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The compute role's LDS ring holds kStages staged KV blocks. Each stage is its own
-// object so the compiler can tell a block copy into one stage from reads of another
-// (it would otherwise wait for every copy in flight before any LDS read). A staging
-// task borrows the same memory as scratch for its transposes.
-__shared__ __attribute__((aligned(16))) uint8_t g_stage0[Block<128>::kBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage1[Block<128>::kBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage2[Block<128>::kBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage3[Block<128>::kBytes];
+// The compute role's LDS ring of kStages staged KV blocks: the K parts of stages 0..3
+// first, then their Vᵀ parts (stage_k / stage_v byte offsets), so every operand read
+// reaches its stage with one per-lane address register and the 16-bit offset field.
+// The compute role reads the ring only through ds_read_b128 in inline asm
+// (lds_read16) with explicit waits: the compiler cannot tell which stage a block copy
+// in flight writes and would otherwise wait for every copy before any LDS read. A
+// staging task borrows the same memory as scratch for its transposes (scratch_buf).
+constexpr int kLdsBytes = kStages * Block<128>::kBytes;
+__shared__ __attribute__((aligned(16))) uint8_t g_lds[kLdsBytes];
 __shared__ int32_t g_cmd[4];
 
-template <int S>
-__device__ __forceinline__ uint8_t* stage_buf() {
-  static_assert(kStages == 4, "one named buffer per stage");
-  if constexpr (S == 0) return g_stage0;
-  else if constexpr (S == 1) return g_stage1;
-  else if constexpr (S == 2) return g_stage2;
-  else return g_stage3;
+template <int D, int S>
+constexpr int stage_k() { return S * Block<D>::kKBytes; }
+template <int D, int S>
+constexpr int stage_v() { return (kStages + S) * Block<D>::kKBytes; }
+
+template <int B>
+__device__ __forceinline__ uint8_t* scratch_buf() {
+  static_assert(B >= 0 && B < 4, "scratch");
+  return g_lds + B * (kLdsBytes / 4);
+}
+
+// LDS byte address of g_lds (the 32-bit offset the ds_* instructions take).
+__device__ __forceinline__ uint32_t lds_base() { return (uint32_t)(uintptr_t)((lds_void*)g_lds); }
+
+// 16 bytes from LDS address addr + OFF (OFF < 65536, the instruction's offset field).
+// The result may only be used after lgkm_wait with a count that covers it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536 && OFF % 16 == 0, "ds_read_b128 offset");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+
+// Waits until at most N LDS reads of this wave are outstanding (LDS operations
+// complete in order, so every read older than the newest N is done); v, the register
+// such a read filled, is tied to the wait so no use of it moves above.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& v) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
 
 // 16-byte chunk positions inside a staged block (see Block<D>).
@@ -287,7 +323,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 // to fp16. The slot is free once every unit has finished step t - 2. One release per
 // tile publishes its epoch-stamped flag (paper §4: epoch-stamped readiness flags).
 template <int D>
-__device__ void stage_tile(const KernelArgs& a, uint32_t k, bool assist) {
+__device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k, bool assist) {
   constexpr int CPR = D / 8;                        // 16-byte chunks per K/V row
   constexpr int KCH = kBN * CPR / kThreads;         // K (or V) chunks per thread per block
   constexpr int VPITCH = kBN + 2;                   // fp16 scratch row pitch (breaks bank conflicts)
@@ -327,7 +363,7 @@ __device__ void stage_tile(const KernelArgs& a, uint32_t k, bool assist) {
           vr[b][i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + off)) : u32x4{0, 0, 0, 0};
         }
       }
-      uint8_t* scr[NB] = {g_stage0, g_stage1, g_stage2, g_stage3};
+      uint8_t* scr[NB] = {scratch_buf<0>(), scratch_buf<1>(), scratch_buf<2>(), scratch_buf<3>()};
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int p = p0 + b;
@@ -402,32 +438,125 @@ __device__ void stage_tile(const KernelArgs& a, uint32_t k, bool assist) {
     add32(&a.ctrl->stage_done.v, 1);
     add64(&a.ctrl->stage_wait_ticks.v, w);
     if (assist) add32(&a.ctrl->assist_tasks.v, 1);
-    trace_rec(kernel_args(), kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
+    trace_rec(ap, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
   }
   (void)lane;
 }
 
 // ------------------------------------------------------------------ compute role
 
-// Copies staged block `src` (global) into LDS stage S: each wave moves 1 KB per
-// instruction with global_load_lds_dwordx4 (no registers, no VALU).
-template <int D, int S>
-__device__ __forceinline__ void dma_block(const uint8_t* src) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < Block<D>::kChunksPerThread; ++i) {
-    const int ch = i * kThreads + w * 64;
-    __builtin_amdgcn_global_load_lds(src + (int64_t)(ch + lane) * 16, (lds_void*)(stage_buf<S>() + ch * 16), 16, 0, 0);
-  }
+// Copy instruction I of staged block `src` (global) into LDS stage S: each wave
+// moves 1 KB per global_load_lds_dwordx4 (no registers, no VALU); instructions below
+// half the block fill the stage's K part (stage_k), the rest its Vᵀ part (stage_v).
+template <int D, int S, int I>
+__device__ __forceinline__ void dma_one(const uint8_t* src) {
+  constexpr int kHalf = Block<D>::kChunks / 2;  // chunks of the K part
+  static_assert(kHalf % kThreads == 0, "one instruction copies K or V, not both");
+  const int w = (int)wave_bcast(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ch = I * kThreads + w * 64;
+  uint8_t* dst = g_lds + (I * kThreads < kHalf ? stage_k<D, S>() + ch * 16 : stage_v<D, S>() + (ch - kHalf) * 16);
+  __builtin_amdgcn_global_load_lds(src + w * 64 * 16 + I * kThreads * 16 + lane * 16, (lds_void*)dst, 16, 0, 0);
 }
 
+template <int D, int S, int... I>
+__device__ __forceinline__ void dma_seq(const uint8_t* src, std::integer_sequence<int, I...>) {
+  (dma_one<D, S, I>(src), ...);
+}
+
+// The whole block: Block<D>::kChunksPerThread instructions per wave.
+template <int D, int S>
+__device__ __forceinline__ void dma_block(const uint8_t* src) {
+  dma_seq<D, S>(src, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
+}
+
+// Per-lane LDS addresses of the compute role's operand reads (stage 0, block row 0):
+// the K read of k-slice kk and the Vᵀ read of Pᵀ slice pp. Stage and block offsets go
+// in the instruction's offset field.
 template <int D>
-__device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& waited) {
+struct LaneAddr {
+  uint32_t k[D / 16];
+  uint32_t v[4];
+};
+
+// The matrix-core phase of the compute role for block m in stage S: Oᵀ += Vᵀ Pᵀ for
+// block m-1 (stage S-1, when PV) then Sᵀ = K Qᵀ for block m (when QK), as one fixed
+// sequence of MFMAs, each fed by a ds_read_b128 issued LA MFMAs ahead.
+template <int D, int S, bool PV, bool QK>
+struct MPhase {
+  static constexpr int KK = D / 16, DB = D / 32;
+  static constexpr int NPV = PV ? DB * 4 : 0;
+  static constexpr int NQK = QK ? 2 * KK : 0;
+  static constexpr int N = NPV + NQK;
+  static constexpr int LA = MKRA_LDS_AHEAD;  // LDS reads in flight ahead of the MFMA using the oldest
+  static constexpr int R = LA + 2;  // operand registers: a read refills the one used two MFMAs ago
+  static constexpr int SPV = (S + kStages - 1) % kStages;
+
+  template <int J>
+  static constexpr int offset() {
+    if constexpr (J < NPV) return stage_v<D, SPV>() - stage_v<D, 0>() + (J / 4) * 32 * 128;
+    else return stage_k<D, S>() + ((J - NPV) / KK) * 32 * (D * 2);
+  }
+  template <int J>
+  static __device__ __forceinline__ void read(u32x4 (&buf)[R], const LaneAddr<D>& la) {
+    if constexpr (J < N) {
+      if constexpr (J < NPV) buf[J % R] = lds_read16<offset<J>()>(la.v[J % 4]);
+      else buf[J % R] = lds_read16<offset<J>()>(la.k[(J - NPV) % KK]);
+    }
+  }
+  // The copy of the block two ahead (stage S+2), when given, is spread over the
+  // sequence: instruction I after MFMA (2I+1) N / (2 NI), so no wave issues several
+  // copies at once and waits for the memory pipeline to take them.
+  static constexpr int NI = Block<D>::kChunksPerThread;
+  template <int J>
+  static constexpr int dma_at() {
+    for (int i = 0; i < NI; ++i)
+      if (J == (2 * i + 1) * N / (2 * NI)) return i;
+    return -1;
+  }
+  template <int J>
+  static __device__ __forceinline__ void exec(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
+                                              const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
+                                              const uint8_t* dma_src) {
+    constexpr int newer = (N - 1 - J) < (LA - 1) ? (N - 1 - J) : (LA - 1);
+    lgkm_wait<newer>(buf[J % R]);
+    if constexpr (J < NPV) {
+      constexpr int db = J / 4, pp = J % 4;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, buf[J % R]), pb[pp], o[db], 0, 0, 0);
+    } else {
+      constexpr int kb = (J - NPV) / KK, kk = (J - NPV) % KK;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, buf[J % R]), qr[kk],
+                                                      kk == 0 ? f32x16{} : s[kb], 0, 0, 0);
+    }
+    read<J + LA>(buf, la);
+    if constexpr (dma_at<J>() >= 0) {
+      if (dma_src != nullptr) dma_one<D, (S + 2) % kStages, dma_at<J>()>(dma_src);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int... J, int... P>
+  static __device__ __forceinline__ void seq(std::integer_sequence<int, J...>, std::integer_sequence<int, P...>,
+                                             const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
+                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src) {
+    u32x4 buf[R];
+    __builtin_amdgcn_sched_barrier(0);
+    (read<P>(buf, la), ...);
+    (exec<J>(buf, la, o, pb, s, qr, dma_src), ...);
+  }
+  static __device__ __forceinline__ void run(const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
+                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src) {
+    seq(std::make_integer_sequence<int, N>{}, std::make_integer_sequence<int, (LA < N ? LA : N)>{}, la, o, pb, s, qr,
+        dma_src);
+  }
+};
+
+template <int D>
+__device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint64_t& waited) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int NI = Block<D>::kChunksPerThread;  // block-copy instructions per wave per tile
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, col = lane & 31;
+  const int w = (int)wave_bcast((uint32_t)(tid >> 6));  // wave-uniform, kept in SGPRs
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
   const int kvh = p / a.n_hgroups, hgi = p % a.n_hgroups;
   const int h = kvh * a.gqa + hgi * a.hg + (w % a.hg);
@@ -439,8 +568,6 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& wai
   const int q_end = min(a.lq, qb * a.bq + a.bq);
   const int kend = diag ? min(a.lk, q_end) : a.lk;
   const int n_kt = (kend + kBN - 1) / kBN;
-  const int wkend = diag ? min(a.lk, q0w + kRowsPerWave) : a.lk;
-  const int w_kt = wave_rows ? (wkend + kBN - 1) / kBN : 0;
   const float c2 = a.scale_log2;
   bool ok = true;
 
@@ -474,18 +601,16 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& wai
     }
   }
 
-  // Running state: O^T blocks, max (log2 units of the scaled score), and two running
-  // sums: l of the exact P (for the log-sum-exp) and lr of the fp16-rounded P that the
-  // PV product weights V with (for the normalisation, see below).
+  // Running state: Oᵀ blocks, max (log2 units of the scaled score) and the running sum
+  // of P.
   f32x16 o[DB];
-  float m_run, l_run, lr_run;
+  float m_run, l_run;
   float* accw = a.acc + ((int64_t)unit * kWaves + w) * (32 * D + 256);
   if (t == 0) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     m_run = -INFINITY;
     l_run = 0.f;
-    lr_run = 0.f;
   } else {
     const f32x4* a4 = reinterpret_cast<const f32x4*>(accw);
 #pragma unroll
@@ -498,140 +623,195 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& wai
     f32x4 ml = reinterpret_cast<const f32x4*>(accw + 32 * D)[lane];
     m_run = ml[0];
     l_run = ml[1];
-    lr_run = ml[2];
   }
 
-  // Per-lane LDS offsets (the swizzles depend only on the lane).
-  const int k_off = col * (D * 2);                // + kb*32*(D*2) + 16*swz
-  const int kx = (D == 128) ? (col & 15) : ((col >> 1) & 7);
-  const int v_off = Block<D>::kKBytes + col * 128;  // + db*32*128 + 16*swz
-  const int vx = (col >> 1) & 7;
+  // Per-lane LDS addresses (the swizzles depend only on the lane).
+  LaneAddr<D> la;
+  {
+    const uint32_t b0 = lds_base();
+    const int kx = (D == 128) ? (col & 15) : ((col >> 1) & 7);
+    const int vx = (col >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) la.k[kk] = b0 + col * (D * 2) + 16 * ((2 * kk + hi) ^ kx);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) la.v[pp] = b0 + stage_v<D, 0>() + col * 128 + 16 * ((2 * pp + hi) ^ vx);
+  }
 
   auto issue = [&](int kt, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const int j = (kt * kBN) / kStageRows;
     if (j >= ready_upto) {
+      // Wait for this tile's flag, then look at all later flags at once (one load per
+      // lane) so the next few tiles need no check.
       ok &= wave_wait_stamp(a, &flags[j], st, waited);
-      ready_upto = j + 1;
+      int upto = j + 1;
+      for (int j0 = j + 1; j0 < n_st; j0 += 64) {
+        const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
+        const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
+        if (notready) {
+          upto = j0 + (int)__builtin_ctzll(notready);
+          break;
+        }
+        upto = min(n_st, j0 + 64);
+      }
+      if (upto > j + 1) fence_acquire();
+      ready_upto = upto;
     }
     dma_block<D, S>(sblk + (int64_t)kt * Block<D>::kBytes);
   };
 
-  auto compute_tile = [&](int kt, const uint8_t* sb) {
-    // S^T = K Q^T for 2 blocks of 32 keys.
-    f32x16 s[kBN / 32];
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-      s[kb] = f32x16{};
-      const uint8_t* kr = sb + kb * 32 * (D * 2) + k_off;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * kk + hi) ^ kx));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[kk], s[kb], 0, 0, 0);
-      }
-    }
+  // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
+  f32x16 s[kBN / 32];
+  f16x8 pb[kBN / 16];
+
+  // Online-softmax update for block kt (FlashAttention-2), producing fp16 Pᵀ.
+  auto softmax = [&](int kt) {
     // Masks: ragged key tail, and keys after the query on the diagonal step.
     const int k0 = kt * kBN;
     if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
+      // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
+      // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
+      const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
+    }
+    // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
+    // fp32 P (four partial sums, short dependency chains) and the PV product takes P
+    // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
+    // the rounded P would not co-issue with the other wave's MFMAs.)
+    float lsum;
+    auto exp_block = [&](float mref) {
+      float ls[4];
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          int key = k0 + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          if (key >= a.lk || (diag && key > qrow)) s[kb][i] = -INFINITY;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
+          ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
+          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
         }
-    }
-    float mx = -INFINITY;
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    exp_block(m_run);
+    // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
+    // of its P), or on the first block, is the row max of the block needed: raise
+    // m_run to it, rescale O and l, and redo the block. The max the exponentials use
+    // may therefore lag the true max, by at most log2(kSumMax); every P stays in the
+    // fp16 range and the algebra of the online softmax is unchanged.
+    if (__any(!(lsum <= kSumMax))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * c2;
-    // Online-softmax update (FlashAttention-2), rescaling only when the max has grown
-    // by more than kTau since the last rescale.
-    if (__any(mxs > m_run + kTau)) {
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c2);
+      const float alpha = (m_new == m_run || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
+                                                                 : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       l_run *= alpha;
-      lr_run *= alpha;
       m_run = m_new;
+      exp_block(m_run == -INFINITY ? 0.f : m_run);
     }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    f16x8 pb[kBN / 16];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-        lsum += pv;
-        pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
-      }
     l_run += lsum;
-    // lr sums the fp16-rounded P (two per v_dot2c_f32_f16 against (1, 1)); normalising
-    // O by it makes the applied weights sum to one, so a dominant key's rounding
-    // cancels in O / lr.
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < kBN / 16; ++pp) {
-      ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 0, 1), kOnes2, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 2, 3), kOnes2, ls1, false);
-      ls0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 4, 5), kOnes2, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(pb[pp], pb[pp], 6, 7), kOnes2, ls1, false);
+  };
+
+  // Two-phase schedule. Each wave runs M(0) V(0) M(1) V(1) ... M(n_kt), where
+  // M(m) = PV of block m-1 and QKᵀ of block m (matrix cores) and V(m) = the softmax
+  // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
+  // one extra barrier first and group 0 one at the end, so the two waves sharing a
+  // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
+  // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
+  // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
+  // both groups pass only once they are done with it. Before every barrier a wave
+  // waits for its own copies of the next block it or the other group reads; the
+  // barrier then makes every wave's part visible.
+  // Every wave runs every block of the unit: on the diagonal step the blocks past a
+  // wave's last query are fully masked and add exactly zero.
+  int issued = 0;
+  auto wait_block = [&](int need) {
+    const int newer = issued - 1 - need;
+    wait_vm(newer > 0 ? NI : 0);
+  };
+  // M(m): the barrier, the MFMAs, and the copy of block m+2 into stage (S+2)%4.
+  auto mstep = [&](int m, auto stage_tag, auto mfmas) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (m < n_kt) wait_block(m);
+    __builtin_amdgcn_s_barrier();
+    const int kn = m + 2;
+    // Block m+2 is copied during the MFMAs when its staged tile is known to be ready,
+    // else after them (the wait for its flag may block).
+    const bool early = kn < n_kt && (kn * kBN) / kStageRows < ready_upto;
+    mfmas(early ? sblk + (int64_t)kn * Block<D>::kBytes : nullptr);
+    if (early) issued = kn + 1;
+    if (kn < n_kt && !early) {
+      issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
+      issued = kn + 1;
     }
-    lr_run += ls0 + ls1;
-    // O^T += V^T P^T (fp16 operands, fp32 accumulation).
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint8_t* vr = sb + db * 32 * 128 + v_off;
-#pragma unroll
-      for (int pp = 0; pp < kBN / 16; ++pp) {
-        f16x8 av = *reinterpret_cast<const f16x8*>(vr + 16 * ((2 * pp + hi) ^ vx));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[pp], o[db], 0, 0, 0);
+  };
+  auto vstep = [&](int m) {
+    if (m + 1 < n_kt) wait_block(m + 1);
+    __builtin_amdgcn_s_barrier();
+    softmax(m);
+  };
+#define MKRA_PVQK(S) [&](const uint8_t* src) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src); }
+#define MKRA_PV(S) [&](const uint8_t* src) { MPhase<D, S, true, false>::run(la, o, pb, s, qr, src); }
+  if (0 < n_kt) { issue(0, std::integral_constant<int, 0>{}); issued = 1; }
+  if (1 < n_kt) { issue(1, std::integral_constant<int, 1>{}); issued = 2; }
+  if (grp) {
+    wait_block(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  mstep(0, std::integral_constant<int, 0>{},
+        [&](const uint8_t* src) { MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src); });
+  vstep(0);
+  int m = 1;
+  for (; m + 3 < n_kt; m += kStages) {
+    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+    vstep(m);
+    mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+    vstep(m + 1);
+    mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+    vstep(m + 2);
+    mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
+    vstep(m + 3);
+  }
+  if (m < n_kt) {
+    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+    vstep(m);
+    if (++m < n_kt) {
+      mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+      vstep(m);
+      if (++m < n_kt) {
+        mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+        vstep(m);
+        ++m;
       }
     }
-  };
-
-  auto step = [&](int kt, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    if (kt >= n_kt) return;
-    // This wave's copies of tile kt are done once at most the newer tiles' copies
-    // remain; the barrier makes every wave's part visible and frees stage S-1.
-    const int newer = min(kStages - 2, n_kt - 1 - kt);
-    wait_vm(newer * NI);
-    __builtin_amdgcn_s_barrier();
-    // Refill stage S-1 (freed by the barrier) with tile kt+3: now if its staged tile
-    // is known to be ready, else after this tile's compute (the wait may block).
-    const int kn = kt + kStages - 1;
-    const bool early = kn < n_kt && (kn * kBN) / kStageRows < ready_upto;
-    if (early) issue(kn, std::integral_constant<int, (S + kStages - 1) % kStages>{});
-    if (kt < w_kt) compute_tile(kt, stage_buf<S>());
-    if (kn < n_kt && !early) issue(kn, std::integral_constant<int, (S + kStages - 1) % kStages>{});
-  };
-
-  // Prologue: kStages-1 blocks in flight, then one per tile.
-  if (0 < n_kt) issue(0, std::integral_constant<int, 0>{});
-  if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
-  if (2 < n_kt) issue(2, std::integral_constant<int, 2>{});
-  for (int kt = 0; kt < n_kt; kt += kStages) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-    step(kt + 2, std::integral_constant<int, 2>{});
-    step(kt + 3, std::integral_constant<int, 3>{});
   }
+  // M(n_kt): PV of the last block only.
+  switch (n_kt & 3) {
+    case 0: mstep(n_kt, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
+    case 1: mstep(n_kt, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
+    case 2: mstep(n_kt, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
+    default: mstep(n_kt, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
+  }
+#undef MKRA_PVQK
+#undef MKRA_PV
+  if (!grp) __builtin_amdgcn_s_barrier();
 
   if (ok && wave_rows) {
     if (t == a.n_steps - 1) {
-      // Finalise: out = O / lr, lse = ln(2) * (m + log2 l).
+      // Finalise: out = O / l, lse = ln(2) * (m + log2 l).
       const float l_tot = l_run + __shfl_xor(l_run, 32);
-      const float lr_tot = lr_run + __shfl_xor(lr_run, 32);
       if (qrow < a.lq) {
-        const float inv = 1.f / lr_tot;
+        const float inv = 1.f / l_tot;
         uint16_t* op = a.out + ((int64_t)qrow * a.hq + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -654,7 +834,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& wai
         for (int g = 0; g < 4; ++g)
           a4[(db * 4 + g) * 64 + lane] =
               f32x4{o[db][g * 4 + 0], o[db][g * 4 + 1], o[db][g * 4 + 2], o[db][g * 4 + 3]};
-      reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, lr_run, 0.f};
+      reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, 0.f, 0.f};
     }
   }
   // Publish: unit step done (orders the state for step t+1) and slot release. Every
@@ -669,46 +849,172 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, uint64_t& wai
 
 // ------------------------------------------------------------------ scheduling
 
-// Staging task h exists, belongs to a step <= bound, and its slot is already
-// released (every unit has finished step - 2), so running it waits for nothing.
-__device__ __forceinline__ bool stage_claimable(const KernelArgs& a, uint32_t h, int bound) {
-  if ((int)h >= a.n_stage_tasks) return false;
-  const int step = (int)h / a.n_tiles;
-  return step <= bound && (step < 2 || ld32(&a.done_count[step - 2]) >= (uint32_t)a.n_units);
-}
+// Scheduler state of a workgroup (thread 0 only), kept in LDS.
+struct Sched {
+  int32_t role;     // kRoleCompute / kRoleStage
+  int32_t pending;  // a claimed compute task not yet run
+  int32_t pend_u, pend_t;
+};
 
-// Claim the next compute task. Each XCD has a queue of the units of its head groups,
-// step-major, so units that read the same KV head share an L2. A workgroup takes
-// from its own queue only while that queue is at most one step ahead of the slowest
-// queue, else from the slowest queue: every claimed task then needs only staging of
-// steps whose slot release depends on tasks already claimed, so the schedule cannot
-// deadlock whatever subset of workgroups is resident. Run by one lane.
-__device__ __noinline__ bool claim_compute(const KernelArgs* ap, int& unit, int& step) {
+// Picks the workgroup's next task and writes (op, x, y) to cmd. Run by thread 0.
+//
+// Every control word is loaded in one batch first, so a decision costs one memory
+// round trip plus, for a compute task, one compare-and-swap (these words are shared
+// by all XCDs, so each access goes to memory).
+//
+// Compute tasks: each XCD has a queue of the units of its head groups, step-major, so
+// units that read the same KV head share an L2. A workgroup takes from its own queue
+// only while that queue is at most one step ahead of the slowest queue, else from the
+// slowest queue: every claimed task then needs only staging of steps whose slot
+// release depends on tasks already claimed, so the schedule cannot deadlock whatever
+// subset of workgroups is resident. Within a step a queue runs its units from the
+// last, so on the causal diagonal step the longest query blocks start first.
+//
+// Roles change at task boundaries (§3.2): a staging workgroup leaves the role when
+// staging is done or the controller's target dropped below the count; a compute
+// workgroup joins when the count is below the target. The stall rule of §3.2: while
+// staging work that a claimed compute task depends on is unclaimed (tasks of steps up
+// to its own whose slot is already released), the workgroup does that work first.
+__device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_t* cmd) {
   const KernelArgs& a = *ap;
-  const int own = (int)(blockIdx.x % (unsigned)a.n_xcd);
-  for (int attempt = 0; attempt < 1 << 20; ++attempt) {
-    if (has_error(a)) return false;
-    int min_step = a.n_steps, min_x = -1;
-    uint32_t heads[kMaxXcd];
-    int steps[kMaxXcd];
-    for (int x = 0; x < a.n_xcd; ++x) {
-      int64_t ux = units_in_queue(a, x);
-      heads[x] = ld32(&a.ctrl->xcd_head[x].v);
-      steps[x] = (ux == 0 || (int64_t)heads[x] >= ux * a.n_steps) ? a.n_steps : (int)(heads[x] / ux);
-      if (steps[x] < min_step) { min_step = steps[x]; min_x = x; }
+  // Wave 0 loads the control words lane-parallel (one instruction, one round trip);
+  // lane 0 then decides.
+  const int lane = threadIdx.x & 63;
+  const uint32_t* src = lane < kMaxXcd ? &a.ctrl->xcd_head[lane].v
+                      : lane == 8      ? &a.ctrl->error.v
+                      : lane == 9      ? &a.ctrl->stage_head.v
+                      : lane == 10     ? &a.ctrl->n_stage.v
+                      : lane == 11     ? &a.ctrl->target.v
+                      : lane == 12     ? reinterpret_cast<const uint32_t*>(&a.ctrl->ctrl_time.v)
+                                       : reinterpret_cast<const uint32_t*>(&a.ctrl->ctrl_time.v) + 1;
+  const uint32_t word = lane < 14 ? ld32(src) : 0u;
+  uint32_t heads[kMaxXcd];
+#pragma unroll
+  for (int i = 0; i < kMaxXcd; ++i) heads[i] = i < a.n_xcd ? (uint32_t)__builtin_amdgcn_readlane((int)word, i) : 0u;
+  const uint32_t err = (uint32_t)__builtin_amdgcn_readlane((int)word, 8);
+  const uint32_t sh = (uint32_t)__builtin_amdgcn_readlane((int)word, 9);
+  const uint32_t ns = (uint32_t)__builtin_amdgcn_readlane((int)word, 10);
+  const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)word, 11);
+  // The two halves of the update time are read separately: a torn value only makes
+  // the controller's compare-and-swap fail once.
+  const uint64_t last = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)word, 12) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)word, 13) << 32);
+  if (lane != 0) return;
+  int32_t op = kOpExit, x = 0, y = 0;
+  if (err != kErrNone) {
+    cmd[0] = kOpExit;
+    return;
+  }
+  maybe_controller(ap, heads, sh, last);
+  const bool stage_left = (int)sh < a.n_stage_tasks;
+  if (!st->pending) {
+    if (st->role == kRoleStage) {
+      if (!stage_left) {
+        add32(&a.ctrl->n_stage.v, (uint32_t)-1);
+        st->role = kRoleCompute;
+      } else if (!a.split_fixed && (int)ns > target_of(a, tgt) && cas32(&a.ctrl->n_stage.v, ns, ns - 1)) {
+        st->role = kRoleCompute;
+        add32(&a.ctrl->role_switches.v, 1);
+        trace_rec(ap, kTraceRole, 0, ns - 1, 0, 0, 0, 0);
+      }
+    } else if (!a.split_fixed && !a.disable_staging && stage_left) {
+      if ((int)ns < target_of(a, tgt) && cas32(&a.ctrl->n_stage.v, ns, ns + 1)) {
+        st->role = kRoleStage;
+        max32(&a.ctrl->max_stage.v, ns + 1);
+        add32(&a.ctrl->role_switches.v, 1);
+        trace_rec(ap, kTraceRole, 1, ns + 1, 0, 0, 0, 0);
+      }
     }
-    if (min_x < 0) return false;  // every queue exhausted
-    int x = (steps[own] < a.n_steps && steps[own] <= min_step + 1) ? own : min_x;
-    if (cas32(&a.ctrl->xcd_head[x].v, heads[x], heads[x] + 1)) {
-      int64_t ux = units_in_queue(a, x);
-      step = (int)(heads[x] / ux);
-      // Within a step, the queue runs its units from the last: on the causal
-      // diagonal step the longest query blocks start first.
-      unit = a.xcd_unit_begin[x + 1] - 1 - (int)(heads[x] % ux);
-      return true;
+    if (st->role == kRoleStage) {
+      const uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
+      if ((int)kk < a.n_stage_tasks) {
+        op = kOpStage;
+        x = (int32_t)kk;
+      } else {
+        add32(&a.ctrl->n_stage.v, (uint32_t)-1);
+        st->role = kRoleCompute;
+      }
+    }
+    if (op == kOpExit && st->role == kRoleCompute) {
+      // Claim a compute task; a failed compare-and-swap returns the queue's head.
+      const int own = (int)(blockIdx.x % (unsigned)a.n_xcd);
+      bool got = false;
+      for (int attempt = 0; attempt < 1 << 16 && !got; ++attempt) {
+        int min_step = a.n_steps, min_x = -1, own_step = a.n_steps;
+        uint32_t own_head = 0, min_head = 0;
+#pragma unroll
+        for (int q = 0; q < kMaxXcd; ++q) {
+          if (q >= a.n_xcd) break;
+          const int64_t ux = units_in_queue(a, q);
+          const int sq = (ux == 0 || (int64_t)heads[q] >= ux * a.n_steps) ? a.n_steps : (int)(heads[q] / ux);
+          if (q == own) { own_step = sq; own_head = heads[q]; }
+          if (sq < min_step) { min_step = sq; min_x = q; min_head = heads[q]; }
+        }
+        if (min_x < 0) break;  // every queue exhausted
+        const bool mine = own_step < a.n_steps && own_step <= min_step + 1;
+        const int q = mine ? own : min_x;
+        const uint32_t h = mine ? own_head : min_head;
+        uint32_t expect = h;
+        if (__hip_atomic_compare_exchange_strong(&a.ctrl->xcd_head[q].v, &expect, h + 1, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          const int64_t ux = units_in_queue(a, q);
+          st->pend_t = (int32_t)(h / ux);
+          st->pend_u = a.xcd_unit_begin[q + 1] - 1 - (int32_t)(h % ux);
+          got = true;
+        } else {
+#pragma unroll
+          for (int i = 0; i < kMaxXcd; ++i)
+            if (i == q) heads[i] = expect;
+          if (ld32(&a.ctrl->error.v) != kErrNone) break;
+        }
+      }
+      if (got) {
+        st->pending = 1;
+      } else if (stage_left && !a.disable_staging) {
+        // No compute task left to claim: help drain the remaining staging.
+        const uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
+        if ((int)kk < a.n_stage_tasks) {
+          op = kOpStage;
+          x = (int32_t)kk;
+        }
+      }
     }
   }
-  return false;
+  if (st->pending) {
+    // A failed compare-and-swap returns the staging head; retry while the task it
+    // names is still one the stall rule allows.
+    uint32_t h = sh;
+    bool assist = false;
+    int released_below = 0;  // steps whose slot is known released
+    for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
+      const int step = (int)h / a.n_tiles;
+      if (step > st->pend_t) break;
+      if (step >= 2 && step >= released_below) {
+        if (ld32(&a.done_count[step - 2]) < (uint32_t)a.n_units) break;
+        released_below = step + 1;
+      }
+      uint32_t expect = h;
+      if (__hip_atomic_compare_exchange_strong(&a.ctrl->stage_head.v, &expect, h + 1, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        assist = true;
+        break;
+      }
+      h = expect;
+    }
+    if (assist) {
+      op = kOpStage;
+      x = (int32_t)h;
+      y = 1;
+    } else {
+      op = kOpCompute;
+      x = st->pend_u;
+      y = st->pend_t;
+      st->pending = 0;
+    }
+  }
+  cmd[0] = op;
+  cmd[1] = x;
+  cmd[2] = y;
 }
 
 template <int D>
@@ -723,92 +1029,34 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       max32(&a.ctrl->max_stage.v, n);
     }
   }
-  // A claimed compute task not yet run (thread 0 only).
-  bool pending = false;
-  int32_t pend_u = 0, pend_t = 0;
+  // Phase group of this wave (see compute_task): the second wave to land on a SIMD
+  // runs the opposite phase of the first. HW_ID bits 5:4 hold the SIMD of the wave.
+  __shared__ int32_t simd_of_wave[kWaves];
+  int grp;
+  {
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) simd_of_wave[w] = (int32_t)__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));
+    __syncthreads();
+    int before = 0;
+    for (int v = 0; v < w; ++v) before += simd_of_wave[v] == simd_of_wave[w];
+    grp = before & 1;
+  }
+  __shared__ Sched sched;
+  if (tid == 0) {
+    sched.role = (int32_t)role;
+    sched.pending = 0;
+  }
 
   while (true) {
     __syncthreads();
-    if (tid == 0) {
-      int32_t op = kOpExit, x = 0, y = 0;
-      if (!has_error(a)) {
-        maybe_controller(kernel_args());
-        const bool stage_left = (int)ld32(&a.ctrl->stage_head.v) < a.n_stage_tasks;
-        if (!pending) {
-          // Role changes happen at task boundaries (§3.2): leave the staging role when
-          // staging is done or the target dropped below the count; join it when the
-          // count is below the target.
-          if (role == kRoleStage) {
-            uint32_t ns = ld32(&a.ctrl->n_stage.v);
-            if (!stage_left) {
-              add32(&a.ctrl->n_stage.v, (uint32_t)-1);
-              role = kRoleCompute;
-            } else if (!a.split_fixed && (int)ns > current_target(a) && cas32(&a.ctrl->n_stage.v, ns, ns - 1)) {
-              role = kRoleCompute;
-              add32(&a.ctrl->role_switches.v, 1);
-              trace_rec(kernel_args(), kTraceRole, 0, ns - 1, 0, 0, 0, 0);
-            }
-          } else if (!a.split_fixed && !a.disable_staging && stage_left) {
-            uint32_t ns = ld32(&a.ctrl->n_stage.v);
-            if ((int)ns < current_target(a) && cas32(&a.ctrl->n_stage.v, ns, ns + 1)) {
-              role = kRoleStage;
-              max32(&a.ctrl->max_stage.v, ns + 1);
-              add32(&a.ctrl->role_switches.v, 1);
-              trace_rec(kernel_args(), kTraceRole, 1, ns + 1, 0, 0, 0, 0);
-            }
-          }
-          if (role == kRoleStage) {
-            uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
-            if ((int)kk < a.n_stage_tasks) {
-              op = kOpStage;
-              x = (int32_t)kk;
-            } else {
-              add32(&a.ctrl->n_stage.v, (uint32_t)-1);
-              role = kRoleCompute;
-            }
-          }
-          if (op == kOpExit && role == kRoleCompute) {
-            if (claim_compute(kernel_args(), pend_u, pend_t)) {
-              pending = true;
-            } else if (stage_left && !a.disable_staging) {
-              // No compute task left to claim: help drain the remaining staging.
-              uint32_t kk = add32(&a.ctrl->stage_head.v, 1);
-              if ((int)kk < a.n_stage_tasks) {
-                op = kOpStage;
-                x = (int32_t)kk;
-              }
-            }
-          }
-        }
-        if (pending) {
-          // Stall rule of §3.2: while staging work that the claimed task depends on is
-          // unclaimed (tasks of steps up to its own whose slot is already released),
-          // the compute workgroup does that work first; once every such task is
-          // claimed, the data its task waits for is in the hands of running waves.
-          uint32_t h = ld32(&a.ctrl->stage_head.v);
-          if (!a.disable_staging && stage_claimable(a, h, pend_t) && cas32(&a.ctrl->stage_head.v, h, h + 1)) {
-            op = kOpStage;
-            x = (int32_t)h;
-            y = 1;
-          } else {
-            op = kOpCompute;
-            x = pend_u;
-            y = pend_t;
-            pending = false;
-          }
-        }
-      }
-      g_cmd[0] = op;
-      g_cmd[1] = x;
-      g_cmd[2] = y;
-    }
+    if (tid < 64) schedule(kernel_args(), &sched, g_cmd);
     __syncthreads();
     const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
     if (op == kOpExit) break;
     if (op == kOpCompute) {
       const uint64_t t0 = ticks();
       uint64_t w0 = 0;
-      compute_task<D>(a, x, y, w0);
+      compute_task<D>(a, x, y, grp, w0);
       if (tid == 0) {
         const uint64_t busy = ticks() - t0 - w0;
         add64(&a.ctrl->compute_ticks.v, busy);
@@ -817,8 +1065,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
         trace_rec(kernel_args(), kTraceCompute, x, y, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
-      stage_tile<D>(a, (uint32_t)x, y != 0);
-      if (tid == 0) maybe_controller(kernel_args());
+      stage_tile<D>(a, kernel_args(), (uint32_t)x, y != 0);
     }
   }
 
