@@ -445,28 +445,30 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
 
 // ------------------------------------------------------------------ compute role
 
-// Copy instruction I of staged block `src` (global) into LDS stage S: each wave
-// moves 1 KB per global_load_lds_dwordx4 (no registers, no VALU); instructions below
-// half the block fill the stage's K part (stage_k), the rest its Vᵀ part (stage_v).
+// Copy instruction I of a staged block into LDS stage S: each wave moves 1 KB per
+// global_load_lds_dwordx4 (no registers, no VALU); instructions below half the block
+// fill the stage's K part (stage_k), the rest its Vᵀ part (stage_v). src_w is the
+// block's address plus this wave's 1 KB offset, ldsw the same offset in LDS and
+// lane16 = 16 * lane: all three are computed once per task.
 template <int D, int S, int I>
-__device__ __forceinline__ void dma_one(const uint8_t* src) {
+__device__ __forceinline__ void dma_one(const uint8_t* src_w, uint32_t lane16, int ldsw) {
   constexpr int kHalf = Block<D>::kChunks / 2;  // chunks of the K part
   static_assert(kHalf % kThreads == 0, "one instruction copies K or V, not both");
-  const int w = (int)wave_bcast(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int ch = I * kThreads + w * 64;
-  uint8_t* dst = g_lds + (I * kThreads < kHalf ? stage_k<D, S>() + ch * 16 : stage_v<D, S>() + (ch - kHalf) * 16);
-  __builtin_amdgcn_global_load_lds(src + w * 64 * 16 + I * kThreads * 16 + lane * 16, (lds_void*)dst, 16, 0, 0);
+  constexpr int kDst = I * kThreads < kHalf ? stage_k<D, S>() + I * kThreads * 16
+                                            : stage_v<D, S>() + (I * kThreads - kHalf) * 16;
+  __builtin_amdgcn_global_load_lds(src_w + I * kThreads * 16 + lane16, (lds_void*)(g_lds + kDst + ldsw), 16, 0, 0);
 }
 
 template <int D, int S, int... I>
-__device__ __forceinline__ void dma_seq(const uint8_t* src, std::integer_sequence<int, I...>) {
-  (dma_one<D, S, I>(src), ...);
+__device__ __forceinline__ void dma_seq(const uint8_t* src_w, uint32_t lane16, int ldsw,
+                                        std::integer_sequence<int, I...>) {
+  (dma_one<D, S, I>(src_w, lane16, ldsw), ...);
 }
 
 // The whole block: Block<D>::kChunksPerThread instructions per wave.
 template <int D, int S>
-__device__ __forceinline__ void dma_block(const uint8_t* src) {
-  dma_seq<D, S>(src, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
+__device__ __forceinline__ void dma_block(const uint8_t* src_w, uint32_t lane16, int ldsw) {
+  dma_seq<D, S>(src_w, lane16, ldsw, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
 }
 
 // Per-lane LDS addresses of the compute role's operand reads (stage 0, block row 0):
@@ -516,7 +518,7 @@ struct MPhase {
   template <int J>
   static __device__ __forceinline__ void exec(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
                                               const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
-                                              const uint8_t* dma_src) {
+                                              const uint8_t* dma_src, uint32_t lane16, int ldsw) {
     constexpr int newer = (N - 1 - J) < (LA - 1) ? (N - 1 - J) : (LA - 1);
     lgkm_wait<newer>(buf[J % R]);
     if constexpr (J < NPV) {
@@ -529,23 +531,25 @@ struct MPhase {
     }
     read<J + LA>(buf, la);
     if constexpr (dma_at<J>() >= 0) {
-      if (dma_src != nullptr) dma_one<D, (S + 2) % kStages, dma_at<J>()>(dma_src);
+      if (dma_src != nullptr) dma_one<D, (S + 2) % kStages, dma_at<J>()>(dma_src, lane16, ldsw);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   template <int... J, int... P>
   static __device__ __forceinline__ void seq(std::integer_sequence<int, J...>, std::integer_sequence<int, P...>,
                                              const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
-                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src) {
+                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+                                             uint32_t lane16, int ldsw) {
     u32x4 buf[R];
     __builtin_amdgcn_sched_barrier(0);
     (read<P>(buf, la), ...);
-    (exec<J>(buf, la, o, pb, s, qr, dma_src), ...);
+    (exec<J>(buf, la, o, pb, s, qr, dma_src, lane16, ldsw), ...);
   }
   static __device__ __forceinline__ void run(const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
-                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src) {
+                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+                                             uint32_t lane16, int ldsw) {
     seq(std::make_integer_sequence<int, N>{}, std::make_integer_sequence<int, (LA < N ? LA : N)>{}, la, o, pb, s, qr,
-        dma_src);
+        dma_src, lane16, ldsw);
   }
 };
 
@@ -637,6 +641,10 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     for (int pp = 0; pp < 4; ++pp) la.v[pp] = b0 + stage_v<D, 0>() + col * 128 + 16 * ((2 * pp + hi) ^ vx);
   }
 
+  // Per-task copy addressing: this wave's 1 KB slice of every copy instruction.
+  const uint8_t* const sblk_w = sblk + w * 64 * 16;
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const int ldsw = w * 64 * 16;
   auto issue = [&](int kt, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const int j = (kt * kBN) / kStageRows;
@@ -657,7 +665,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
       if (upto > j + 1) fence_acquire();
       ready_upto = upto;
     }
-    dma_block<D, S>(sblk + (int64_t)kt * Block<D>::kBytes);
+    dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, lane16, ldsw);
   };
 
   // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
@@ -748,7 +756,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     // Block m+2 is copied during the MFMAs when its staged tile is known to be ready,
     // else after them (the wait for its flag may block).
     const bool early = kn < n_kt && (kn * kBN) / kStageRows < ready_upto;
-    mfmas(early ? sblk + (int64_t)kn * Block<D>::kBytes : nullptr);
+    mfmas(early ? sblk_w + (int64_t)kn * Block<D>::kBytes : nullptr);
     if (early) issued = kn + 1;
     if (kn < n_kt && !early) {
       issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
@@ -760,8 +768,8 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     __builtin_amdgcn_s_barrier();
     softmax(m);
   };
-#define MKRA_PVQK(S) [&](const uint8_t* src) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src); }
-#define MKRA_PV(S) [&](const uint8_t* src) { MPhase<D, S, true, false>::run(la, o, pb, s, qr, src); }
+#define MKRA_PVQK(S) [&](const uint8_t* src) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, lane16, ldsw); }
+#define MKRA_PV(S) [&](const uint8_t* src) { MPhase<D, S, true, false>::run(la, o, pb, s, qr, src, lane16, ldsw); }
   if (0 < n_kt) { issue(0, std::integral_constant<int, 0>{}); issued = 1; }
   if (1 < n_kt) { issue(1, std::integral_constant<int, 1>{}); issued = 2; }
   if (grp) {
@@ -769,7 +777,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     __builtin_amdgcn_s_barrier();
   }
   mstep(0, std::integral_constant<int, 0>{},
-        [&](const uint8_t* src) { MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src); });
+        [&](const uint8_t* src) { MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, lane16, ldsw); });
   vstep(0);
   int m = 1;
   for (; m + 3 < n_kt; m += kStages) {
