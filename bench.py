@@ -1,14 +1,15 @@
 """Benchmark of the per-rank ring-attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--sweep] [--verify] [--copy-calibration-mib M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--workload NAME]
+                    [--no-cpu-baseline] [--sweep] [--size-sweep] [--verify] [--copy-calibration-mib M]
     python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
 
 A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
 rank, staging included) over one batch of synthetic input already resident in HBM.
 W untimed warm-up calls, then K calls enqueued back to back on one stream with one
 synchronisation at the end (the measurement protocol of the mKernel paper, §5.1),
-timed with HIP events recorded on that stream. Prints ONE JSON line on stdout.
+timed with HIP events recorded on that stream; the K calls are also timed in R groups
+(median and min per launch). Prints ONE JSON line on stdout.
 
 The default workload is the per-rank share of a 64K-token causal GQA sequence over
 16 ranks (rank 15: the slowest rank of a contiguous causal ring). Throughput counts
@@ -19,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s and % bf16 MFMA peak, per-rank ring-attn fwd, 1 MI355X"
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_CLOCK_GHZ = 2.4      # the clock the dense bf16 peak is quoted at
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["overlap_attention_amd/csrc/mkra_kernel.hip", "overlap_attention_amd/csrc/mkra_args.h"]
 
@@ -116,6 +119,85 @@ def write_traffic(cfg, pmc_dir, copy_mib):
         f"(FETCH x{res['FETCH_SIZE']['scale']:.3f}, WRITE x{res['WRITE_SIZE']['scale']:.3f})")
 
 
+def staging_summary(cfg, stats, ms):
+    """The staging role's traffic: every step's chunk read once from its home and
+    written once into the double buffer, in tiles of 128 rows."""
+    chunk = 2 * cfg.lk * cfg.hkv * cfg.d * 2
+    moved = 2 * cfg.n_steps * chunk  # read + write
+    busy_s = stats["staging_busy_ticks"] * 1e-8
+    return {
+        "initial_target": stats["initial_target"],
+        "final_target": stats["final_target"],
+        "max_staging_wgs": stats["max_staging_wgs"],
+        "grid_wgs": stats["grid_wgs"],
+        "tasks": stats["staging_tasks_done"],
+        "assisted_tasks": stats["assist_tasks"],
+        "bytes_per_launch": moved,
+        "gbs_over_launch": round(moved / (ms * 1e-3) / 1e9, 1),
+        "gbs_per_busy_wg": round(moved / busy_s / 1e9, 1) if busy_s > 0 else None,
+    }
+
+
+SPLITS = (1, 2, 4, 8, 16, 32, 64)
+
+
+def split_sweep(mk, timed, k):
+    """Fixed numbers of staging workgroups against the adaptive controller: ms per
+    launch and each one's latency relative to the best fixed split (Fig. 3 of the
+    paper plots this ratio)."""
+    res = {}
+    for n in SPLITS:
+        res[f"fixed{n}"] = timed(k, mk.default_opts(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n))[0]
+    res["adaptive"] = timed(k)[0]
+    best_name = min((n for n in res if n != "adaptive"), key=lambda n: res[n])
+    return {"ms": {n: round(v, 4) for n, v in res.items()}, "best_fixed": best_name,
+            "best_fixed_ms": round(res[best_name], 4), "adaptive_over_best": round(res["adaptive"] / res[best_name], 3)}
+
+
+def run_size_sweep(torch, mk, make_inputs, stream):
+    """The split sweep over total sequence sizes 6K..192K (the range of Fig. 3): rank
+    15 of a 16-rank causal GQA ring, Hq = 32, Hkv = 8, D = 128."""
+    from ring_inputs import RingConfig
+
+    out = []
+    for total in (6144, 12288, 24576, 49152, 98304, 196608):
+        L = total // 16
+        cfg = RingConfig(f"seq{total // 1024}k_r15of16_L{L}_h32kv8_d128_causal", rank=15, n_chunks=16, lq=L, lk=L,
+                         hq=32, hkv=8, d=128, causal=True)
+        q, kv = make_inputs(cfg, seed=7)
+        qg, kvg = q.cuda(), kv.cuda()
+        del q, kv
+        o = torch.empty_like(qg)
+        l = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device="cuda")
+
+        def timed_cfg(k, opts=None, groups=1):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for _ in range(2):
+                mk.mk_ring_attn_fwd_ex(qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, o, l,
+                                       stream=stream, opts=opts)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(k):
+                mk.mk_ring_attn_fwd_ex(qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, o, l,
+                                       stream=stream, opts=opts)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / k, None
+
+        k = max(3, int(60 / max(1.0, (L / 4096) ** 2 * 4.2)))
+        sw = split_sweep(mk, timed_cfg, k)
+        mk.mk_ring_attn_status()
+        sw["tflops_adaptive"] = round(algorithmic_flops(cfg) / (sw["ms"]["adaptive"] * 1e-3) / 1e12, 1)
+        sw["total_seq"] = total
+        sw["chunk_rows"] = L
+        out.append(sw)
+        log(f"[bench] size {total}: adaptive {sw['ms']['adaptive']:.3f} ms ({sw['tflops_adaptive']} TFLOP/s), "
+            f"best fixed {sw['best_fixed']} {sw['best_fixed_ms']:.3f} ms, adaptive/best {sw['adaptive_over_best']}")
+        del qg, kvg, o, l
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, q, kv, budget_rows):
     """The fp64 oracle on the host cores, on a bounded sample of the same workload:
     `budget_rows` query rows spread over the chunk, all heads, all keys."""
@@ -167,7 +249,11 @@ def main():
     ap.add_argument("--workload", default=None, help="name of a workload in ring_inputs.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536)
-    ap.add_argument("--sweep", action="store_true", help="also time fixed staging splits vs adaptive (stderr)")
+    ap.add_argument("--repeats", type=int, default=5, help="groups the timed launches are split into (median, min)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time fixed staging splits {1..64} against the adaptive split (Fig. 3's metric)")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="also run the split sweep over total sequence sizes 6K..192K (16 ranks, rank 15)")
     ap.add_argument("--verify", action="store_true", help="check sampled rows against the oracle (stderr)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), the known-size "
@@ -208,15 +294,22 @@ def main():
             mk.mk_ring_attn_fwd_ex(qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, out, lse,
                                    stream=stream, opts=opts)
 
-    def timed(k, opts=None):
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed(k, opts=None, groups=1):
+        """Mean ms per launch over k launches back to back on the stream, and the
+        per-launch time of each of `groups` consecutive groups of them (HIP events
+        recorded on the same stream between the groups)."""
+        groups = max(1, min(groups, k))
+        sizes = [k // groups + (1 if i < k % groups else 0) for i in range(groups)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
         torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(k):
-            step(opts)
-        ev1.record(stream)
+        evs[0].record(stream)
+        for g, n in enumerate(sizes):
+            for _ in range(n):
+                step(opts)
+            evs[g + 1].record(stream)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / k  # ms per launch
+        per_group = [evs[g].elapsed_time(evs[g + 1]) / n for g, n in enumerate(sizes)]
+        return evs[0].elapsed_time(evs[-1]) / k, per_group
 
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
@@ -233,12 +326,15 @@ def main():
     mk.mk_ring_attn_status()
     log(f"[bench] timing {args.steps} launches")
     t_host0 = time.perf_counter()
-    ms = timed(args.steps)
+    ms, per_group = timed(args.steps, groups=args.repeats)
     t_host = time.perf_counter() - t_host0
+    ms_median = statistics.median(per_group)
+    ms_min = min(per_group)
     mk.mk_ring_attn_status()
     flops = algorithmic_flops(cfg)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/launch, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
+        f"groups of {args.steps // max(1, args.repeats)}: median {ms_median:.3f} ms, min {ms_min:.3f} ms; "
         f"host wall {t_host:.3f} s")
 
     stats = mk.ring_attn_fwd(qg, kvg, cfg.rank, cfg.causal, cfg.gqa_ratio, want_stats=True)[2]
@@ -254,17 +350,20 @@ def main():
         rep = compare(to_f64(out[rows]), lse[:, rows].double().cpu().numpy(), ro, rl)
         log(f"[bench] verify: {fmt(rep)}")
 
+    sweep = None
     if args.sweep:
-        res = {}
-        for n in (1, 2, 4, 8, 16, 32, 64):
-            res[f"fixed{n}"] = timed(max(3, args.steps // 3), mk.default_opts(split_mode=mk.MK_SPLIT_FIXED,
-                                                                             fixed_staging_wgs=n))
-        res["adaptive"] = timed(max(3, args.steps // 3))
-        best = min(v for k, v in res.items() if k != "adaptive")
+        sweep = split_sweep(mk, timed, max(3, args.steps // 3))
         log("[bench] sweep (ms/launch, latency / best fixed): " +
-            ", ".join(f"{k}={v:.3f} ({v / best:.2f}x)" for k, v in res.items()))
+            ", ".join(f"{k}={v:.3f} ({v / sweep['best_fixed_ms']:.2f}x)" for k, v in sweep["ms"].items()))
+    size_sweep = None
+    if args.size_sweep:
+        size_sweep = run_size_sweep(torch, mk, make_inputs, stream)
 
     traffic = stored_traffic(cfg.name)
+    # Average shader clock over every workgroup's lifetime (s_memtime cycles against
+    # 100 MHz ticks), and the MFMA peak scaled to it: the fraction the schedule
+    # reaches at the clock the chip actually ran, next to the one at 2.4 GHz.
+    clock_ghz = (stats["wg_cycles"] / stats["wg_ticks"] * 0.1) if stats["wg_ticks"] > 0 else None
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -299,14 +398,18 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(cfg),
             "kernel": "mkra::ring_attn_kernel<%d>" % cfg.d,
+            "shader_clock_ghz": round(clock_ghz, 3) if clock_ghz else None,
+            "frac_at_shader_clock": (round(tflops / (PEAK_BF16_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ), 4)
+                                     if clock_ghz else None),
         },
-        "staging": {
-            "initial_target": stats["initial_target"],
-            "final_target": stats["final_target"],
-            "max_staging_wgs": stats["max_staging_wgs"],
-            "grid_wgs": stats["grid_wgs"],
-        },
+        "timing": {"groups": args.repeats, "median_ms_per_step": round(ms_median, 4),
+                   "min_ms_per_step": round(ms_min, 4)},
+        "staging": staging_summary(cfg, stats, ms),
     }
+    if sweep is not None:
+        line["split_sweep"] = sweep
+    if size_sweep is not None:
+        line["size_sweep"] = size_sweep
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
         line["cpu_baseline"] = cpu_baseline(cfg, q, kv, args.cpu_rows)

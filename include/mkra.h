@@ -121,7 +121,11 @@ typedef struct {
   int64_t kernel_ticks;        /* first workgroup start to last workgroup exit */
   int64_t trace_records;       /* records written (may exceed trace_capacity) */
   int64_t debug_mismatches;    /* see mk_ring_attn_opts.debug_flags */
-  int64_t reserved[3];
+  int64_t wg_cycles;           /* shader-clock cycles (s_memtime) of every workgroup's
+                                  lifetime, summed */
+  int64_t wg_ticks;            /* the same lifetimes in 100 MHz ticks: the average
+                                  shader clock is wg_cycles / wg_ticks * 100 MHz */
+  int64_t reserved[1];
 } mk_ring_attn_stats;
 
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,

@@ -70,7 +70,9 @@ class mk_ring_attn_stats(ctypes.Structure):
         ("kernel_ticks", ctypes.c_int64),
         ("trace_records", ctypes.c_int64),
         ("debug_mismatches", ctypes.c_int64),
-        ("reserved", ctypes.c_int64 * 3),
+        ("wg_cycles", ctypes.c_int64),
+        ("wg_ticks", ctypes.c_int64),
+        ("reserved", ctypes.c_int64 * 1),
     ]
 
     def as_dict(self):

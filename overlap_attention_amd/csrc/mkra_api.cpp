@@ -383,6 +383,8 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     stats->kernel_ticks = ds.kernel_ticks;
     stats->trace_records = ds.trace_records;
     stats->debug_mismatches = ds.debug_mismatch;
+    stats->wg_cycles = ds.wg_cycles;
+    stats->wg_ticks = ds.wg_ticks;
   }
   return MK_OK;
 }

@@ -72,6 +72,8 @@ struct DevCtrl {
   Line32 debug_mismatch;      // debug: staged vectors that differed from their source
   Line64 t_first;             // min start tick (0 = unset)
   Line64 t_last;              // max exit tick
+  Line64 wg_cycles;           // shader-clock cycles (s_memtime) summed over workgroups
+  Line64 wg_ticks;            // the same spans in 100 MHz ticks
 };
 
 // Survives launches: the host reads it after a call.
@@ -93,6 +95,8 @@ struct DevStatus {
   int64_t kernel_ticks;
   int64_t trace_records;
   int64_t debug_mismatch;
+  int64_t wg_cycles;
+  int64_t wg_ticks;
 };
 
 struct TraceRec {

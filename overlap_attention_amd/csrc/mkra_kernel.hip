@@ -1029,6 +1029,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   const int tid = threadIdx.x;
   const uint64_t t_start = ticks();
+  const uint64_t c_start = __builtin_readcyclecounter();  // s_memtime: shader clock
   uint32_t role = ((int)blockIdx.x < a.initial_stagers) ? kRoleStage : kRoleCompute;
   if (tid == 0) {
     max64(&a.ctrl->t_first.v, ~t_start);  // stores the complement: max of ~t = min t
@@ -1081,7 +1082,10 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   // block for the next launch on this workspace.
   __shared__ int last;
   if (tid == 0) {
-    max64(&a.ctrl->t_last.v, ticks());
+    const uint64_t t_end = ticks();
+    add64(&a.ctrl->wg_cycles.v, __builtin_readcyclecounter() - c_start);
+    add64(&a.ctrl->wg_ticks.v, t_end - t_start);
+    max64(&a.ctrl->t_last.v, t_end);
     fence_release();
     uint32_t n = __hip_atomic_fetch_add(&a.ctrl->exit_count.v, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     last = (n == (uint32_t)a.grid - 1);
@@ -1110,6 +1114,8 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
     ds->kernel_ticks = (int64_t)(ld64(&cb->t_last.v) - ~ld64(&cb->t_first.v));
     ds->trace_records = (int64_t)ld32(&cb->trace_head.v);
     ds->debug_mismatch = (int64_t)ld32(&cb->debug_mismatch.v);
+    ds->wg_cycles = (int64_t)ld64(&cb->wg_cycles.v);
+    ds->wg_ticks = (int64_t)ld64(&cb->wg_ticks.v);
   }
   __syncthreads();
   uint32_t* words = reinterpret_cast<uint32_t*>(cb);
