@@ -445,30 +445,48 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
 
 // ------------------------------------------------------------------ compute role
 
+// A 64-bit pointer that is the same in every lane, moved to SGPRs.
+__device__ __forceinline__ const uint8_t* wave_bcast_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  return (const uint8_t*)(uintptr_t)(((uint64_t)wave_bcast((uint32_t)(v >> 32)) << 32) | wave_bcast((uint32_t)v));
+}
+
+// Per-lane byte offsets of a wave's block-copy instructions: instruction I moves the
+// 16 bytes at I * kThreads * 16 + 16 * lane of the wave's slice.
+template <int D>
+struct CopyLanes {
+  uint32_t off[Block<D>::kChunksPerThread];
+};
+
 // Copy instruction I of a staged block into LDS stage S: each wave moves 1 KB per
 // global_load_lds_dwordx4 (no registers, no VALU); instructions below half the block
 // fill the stage's K part (stage_k), the rest its Vᵀ part (stage_v). src_w is the
-// block's address plus this wave's 1 KB offset, ldsw the same offset in LDS and
-// lane16 = 16 * lane: all three are computed once per task.
+// block's address plus this wave's 1 KB offset and m0w the LDS address of the same
+// offset in stage 0, both wave-uniform; the instruction takes src_w from SGPRs and the
+// lane's offset from a
+// VGPR computed once per task, so issuing a copy needs no vector ALU work (the matrix
+// phase threads these through its MFMAs, and the vector ALU there belongs to the
+// other wave's softmax).
 template <int D, int S, int I>
-__device__ __forceinline__ void dma_one(const uint8_t* src_w, uint32_t lane16, int ldsw) {
+__device__ __forceinline__ void dma_one(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w) {
   constexpr int kHalf = Block<D>::kChunks / 2;  // chunks of the K part
   static_assert(kHalf % kThreads == 0, "one instruction copies K or V, not both");
   constexpr int kDst = I * kThreads < kHalf ? stage_k<D, S>() + I * kThreads * 16
                                             : stage_v<D, S>() + (I * kThreads - kHalf) * 16;
-  __builtin_amdgcn_global_load_lds(src_w + I * kThreads * 16 + lane16, (lds_void*)(g_lds + kDst + ldsw), 16, 0, 0);
+  const uint32_t m0 = m0w + (uint32_t)kDst;
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(cl.off[I]), "s"(src_w), "{m0}"(m0) : "memory");
 }
 
 template <int D, int S, int... I>
-__device__ __forceinline__ void dma_seq(const uint8_t* src_w, uint32_t lane16, int ldsw,
+__device__ __forceinline__ void dma_seq(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w,
                                         std::integer_sequence<int, I...>) {
-  (dma_one<D, S, I>(src_w, lane16, ldsw), ...);
+  (dma_one<D, S, I>(src_w, cl, m0w), ...);
 }
 
 // The whole block: Block<D>::kChunksPerThread instructions per wave.
 template <int D, int S>
-__device__ __forceinline__ void dma_block(const uint8_t* src_w, uint32_t lane16, int ldsw) {
-  dma_seq<D, S>(src_w, lane16, ldsw, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
+__device__ __forceinline__ void dma_block(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w) {
+  dma_seq<D, S>(src_w, cl, m0w, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
 }
 
 // Per-lane LDS addresses of the compute role's operand reads (stage 0, block row 0):
@@ -482,8 +500,9 @@ struct LaneAddr {
 
 // The matrix-core phase of the compute role for block m in stage S: Oᵀ += Vᵀ Pᵀ for
 // block m-1 (stage S-1, when PV) then Sᵀ = K Qᵀ for block m (when QK), as one fixed
-// sequence of MFMAs, each fed by a ds_read_b128 issued LA MFMAs ahead.
-template <int D, int S, bool PV, bool QK>
+// sequence of MFMAs, each fed by a ds_read_b128 issued LA MFMAs ahead, with one block
+// copy threaded through it (COPY).
+template <int D, int S, bool PV, bool QK, bool COPY = true>
 struct MPhase {
   static constexpr int KK = D / 16, DB = D / 32;
   static constexpr int NPV = PV ? DB * 4 : 0;
@@ -505,9 +524,10 @@ struct MPhase {
       else buf[J % R] = lds_read16<offset<J>()>(la.k[(J - NPV) % KK]);
     }
   }
-  // The copy of the block two ahead (stage S+2), when given, is spread over the
-  // sequence: instruction I after MFMA (2I+1) N / (2 NI), so no wave issues several
-  // copies at once and waits for the memory pipeline to take them.
+  // The copy into stage S+2 is spread over the sequence: instruction I after MFMA
+  // (2I+1) N / (2 NI), so no wave issues several copies at once and waits for the
+  // memory pipeline to take them. It is unconditional (a branch here would put vector
+  // ALU work for its condition into the stream).
   static constexpr int NI = Block<D>::kChunksPerThread;
   template <int J>
   static constexpr int dma_at() {
@@ -518,7 +538,7 @@ struct MPhase {
   template <int J>
   static __device__ __forceinline__ void exec(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
                                               const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
-                                              const uint8_t* dma_src, uint32_t lane16, int ldsw) {
+                                              const uint8_t* dma_src, const CopyLanes<D>& cl, uint32_t m0w) {
     constexpr int newer = (N - 1 - J) < (LA - 1) ? (N - 1 - J) : (LA - 1);
     lgkm_wait<newer>(buf[J % R]);
     if constexpr (J < NPV) {
@@ -530,26 +550,24 @@ struct MPhase {
                                                       kk == 0 ? f32x16{} : s[kb], 0, 0, 0);
     }
     read<J + LA>(buf, la);
-    if constexpr (dma_at<J>() >= 0) {
-      if (dma_src != nullptr) dma_one<D, (S + 2) % kStages, dma_at<J>()>(dma_src, lane16, ldsw);
-    }
+    if constexpr (COPY && dma_at<J>() >= 0) dma_one<D, (S + 2) % kStages, dma_at<J>()>(dma_src, cl, m0w);
     __builtin_amdgcn_sched_barrier(0);
   }
   template <int... J, int... P>
   static __device__ __forceinline__ void seq(std::integer_sequence<int, J...>, std::integer_sequence<int, P...>,
                                              const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
                                              f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
-                                             uint32_t lane16, int ldsw) {
+                                             const CopyLanes<D>& cl, uint32_t m0w) {
     u32x4 buf[R];
     __builtin_amdgcn_sched_barrier(0);
     (read<P>(buf, la), ...);
-    (exec<J>(buf, la, o, pb, s, qr, dma_src, lane16, ldsw), ...);
+    (exec<J>(buf, la, o, pb, s, qr, dma_src, cl, m0w), ...);
   }
   static __device__ __forceinline__ void run(const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
                                              f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
-                                             uint32_t lane16, int ldsw) {
+                                             const CopyLanes<D>& cl, uint32_t m0w) {
     seq(std::make_integer_sequence<int, N>{}, std::make_integer_sequence<int, (LA < N ? LA : N)>{}, la, o, pb, s, qr,
-        dma_src, lane16, ldsw);
+        dma_src, cl, m0w);
   }
 };
 
@@ -561,6 +579,10 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
 
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, col = lane & 31;
   const int w = (int)wave_bcast((uint32_t)(tid >> 6));  // wave-uniform, kept in SGPRs
+  // The task comes through LDS; telling the compiler it is uniform keeps every
+  // address derived from it (slot, head, block) in SGPRs.
+  unit = (int)wave_bcast((uint32_t)unit);
+  t = (int)wave_bcast((uint32_t)t);
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
   const int kvh = p / a.n_hgroups, hgi = p % a.n_hgroups;
   const int h = kvh * a.gqa + hgi * a.hg + (w % a.hg);
@@ -641,10 +663,17 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     for (int pp = 0; pp < 4; ++pp) la.v[pp] = b0 + stage_v<D, 0>() + col * 128 + 16 * ((2 * pp + hi) ^ vx);
   }
 
-  // Per-task copy addressing: this wave's 1 KB slice of every copy instruction.
-  const uint8_t* const sblk_w = sblk + w * 64 * 16;
-  const uint32_t lane16 = (uint32_t)lane * 16u;
-  const int ldsw = w * 64 * 16;
+  // Per-task copy addressing: this wave's 1 KB slice of every copy instruction (base
+  // in SGPRs, per-lane offsets in VGPRs that the compiler may not recompute inside
+  // the matrix phase).
+  const uint8_t* const sblk_w = wave_bcast_ptr(sblk + w * 64 * 16);
+  CopyLanes<D> cl;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    cl.off[i] = (uint32_t)(i * kThreads * 16 + lane * 16);
+    asm volatile("" : "+v"(cl.off[i]));
+  }
+  const uint32_t m0w_task = lds_base() + (uint32_t)w * 64u * 16u;
   auto issue = [&](int kt, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const int j = (kt * kBN) / kStageRows;
@@ -663,9 +692,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
         upto = min(n_st, j0 + 64);
       }
       if (upto > j + 1) fence_acquire();
-      ready_upto = upto;
+      ready_upto = (int)wave_bcast((uint32_t)upto);
     }
-    dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, lane16, ldsw);
+    dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, cl, m0w_task);
   };
 
   // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
@@ -742,42 +771,72 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   // barrier then makes every wave's part visible.
   // Every wave runs every block of the unit: on the diagonal step the blocks past a
   // wave's last query are fully masked and add exactly zero.
-  int issued = 0;
-  auto wait_block = [&](int need) {
-    const int newer = issued - 1 - need;
-    wait_vm(newer > 0 ? NI : 0);
+  //
+  // The compiler may move register-only arithmetic across s_barrier (it orders only
+  // memory), which would pull softmax work into the matrix phase or the reverse and
+  // undo the ping-pong. Empty volatile asm statements, which keep their order with
+  // the barriers, pin each phase's inputs after its barrier and its outputs before
+  // the next one.
+  auto pin_scores = [&]() {
+    if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
   };
-  // M(m): the barrier, the MFMAs, and the copy of block m+2 into stage (S+2)%4.
+  auto pin_acc = [&]() {
+    if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+    else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
+  };
+  auto pin_state = [&]() {
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
+    pin_acc();
+  };
+  // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
+  // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
+  // copy is block m+2 when it exists and its staged tile is known to be ready; else it
+  // copies a valid block (m+2 clamped) whose contents nobody reads, and block m+2, if
+  // it exists, is copied again after the MFMAs once its flag is seen (same wave, same
+  // LDS addresses, completes later). So every wait below has at least one block copy
+  // issued after the one it needs, and waiting until at most NI copy instructions are
+  // outstanding is enough (it may also cover a discarded copy).
+  auto wait_block = [&]() { wait_vm(NI); };
+  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
   auto mstep = [&](int m, auto stage_tag, auto mfmas) {
     constexpr int S = decltype(stage_tag)::value;
-    if (m < n_kt) wait_block(m);
+    if (m < n_kt) wait_block();
     __builtin_amdgcn_s_barrier();
     const int kn = m + 2;
-    // Block m+2 is copied during the MFMAs when its staged tile is known to be ready,
-    // else after them (the wait for its flag may block).
-    const bool early = kn < n_kt && (kn * kBN) / kStageRows < ready_upto;
-    mfmas(early ? sblk_w + (int64_t)kn * Block<D>::kBytes : nullptr);
-    if (early) issued = kn + 1;
-    if (kn < n_kt && !early) {
-      issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
-      issued = kn + 1;
-    }
+    const bool ready = wave_bcast(kn < n_kt && (kn * kBN) / kStageRows < ready_upto) != 0;
+    // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
+    // and instruction offsets here (scalar adds) instead of keeping sixteen of them
+    // in SGPRs across the loop.
+    uint32_t m0w = m0w_task;
+    asm volatile("" : "+s"(m0w));
+    mfmas(sblk_w + (int64_t)min(kn, n_kt - 1) * Block<D>::kBytes, m0w);
+    pin_scores();
+    pin_acc();
+    if (kn < n_kt && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
   };
   auto vstep = [&](int m) {
-    if (m + 1 < n_kt) wait_block(m + 1);
+    if (m + 1 < n_kt) wait_block();
     __builtin_amdgcn_s_barrier();
+    pin_scores();
     softmax(m);
+    pin_state();
   };
-#define MKRA_PVQK(S) [&](const uint8_t* src) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, lane16, ldsw); }
-#define MKRA_PV(S) [&](const uint8_t* src) { MPhase<D, S, true, false>::run(la, o, pb, s, qr, src, lane16, ldsw); }
-  if (0 < n_kt) { issue(0, std::integral_constant<int, 0>{}); issued = 1; }
-  if (1 < n_kt) { issue(1, std::integral_constant<int, 1>{}); issued = 2; }
+#define MKRA_PVQK(S) \
+  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
+#define MKRA_PV(S) \
+  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
+  // n_kt >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
+  // unit's first query).
+  issue(0, std::integral_constant<int, 0>{});
+  if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
+  else dma_block<D, 1>(sblk_w, cl, m0w_task);  // discarded (see the copy rule above)
   if (grp) {
-    wait_block(0);
+    wait_block();
     __builtin_amdgcn_s_barrier();
   }
-  mstep(0, std::integral_constant<int, 0>{},
-        [&](const uint8_t* src) { MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, lane16, ldsw); });
+  mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
+    MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
+  });
   vstep(0);
   int m = 1;
   for (; m + 3 < n_kt; m += kStages) {
@@ -803,7 +862,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
       }
     }
   }
-  // M(n_kt): PV of the last block only.
+  // M(n_kt): PV of the last block only; no wait follows, so it copies nothing.
   switch (n_kt & 3) {
     case 0: mstep(n_kt, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
     case 1: mstep(n_kt, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
@@ -813,6 +872,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
 #undef MKRA_PVQK
 #undef MKRA_PV
   if (!grp) __builtin_amdgcn_s_barrier();
+  // Discarded copies may still be in flight: drain them before this workgroup's next
+  // task (or staging task) writes the same LDS.
+  wait_vm(0);
 
   if (ok && wave_rows) {
     if (t == a.n_steps - 1) {
