@@ -188,7 +188,7 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   int n = eq2_target(a.grid, rp, rs, cp, cs);
   st32(&a.ctrl->target.v, (uint32_t)(n + 1));
   add32(&a.ctrl->ctrl_updates.v, 1);
-  trace_rec(ap, kTraceController, rp, rs, cp, cs, a.grid, n);
+  if (a.trace != nullptr) trace_rec(ap, kTraceController, rp, rs, cp, cs, a.grid, n);
 }
 // ------------------------------------------------------------------ waits
 // All waits are bounded: past timeout_ticks they raise MK_E_TIMEOUT, and every wait
@@ -438,7 +438,7 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
     add32(&a.ctrl->stage_done.v, 1);
     add64(&a.ctrl->stage_wait_ticks.v, w);
     if (assist) add32(&a.ctrl->assist_tasks.v, 1);
-    trace_rec(ap, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
+    if (a.trace != nullptr) trace_rec(ap, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
   }
   (void)lane;
 }
@@ -597,25 +597,8 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   const float c2 = a.scale_log2;
   bool ok = true;
 
-  // Per-unit step order: the state of step t-1 must be complete.
-  if (t > 0) ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t - 1), waited);
-
-  // Ready flags of the staged tiles: one acquire if all are ready already.
-  const uint64_t* flags = a.slot_flags + (t & 1) * a.n_tiles;
-  const uint64_t st = stamp(a.epoch, t);
-  const int n_st = (kend + kStageRows - 1) / kStageRows;
-  int ready_upto = n_st;
-  {
-    bool mine = true;
-    for (int j = lane; j < n_st; j += 64) mine &= (ld64(&flags[j]) == st);
-    if (__all(mine)) {
-      fence_acquire();
-    } else {
-      ready_upto = 0;
-    }
-  }
-
-  // Q: lane holds Q[qrow][h][kk*16 + 8*hi .. +7] for every k-slice.
+  // Q first: it is read-only input, so its loads need no flag and overlap the flag
+  // round trip below. Lane holds Q[qrow][h][kk*16 + 8*hi .. +7] for every k-slice.
   bf16x8 qr[KK];
   {
     const bool in = qrow < a.lq;
@@ -624,6 +607,30 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = in ? *reinterpret_cast<const u32x4*>(qp + kk * 16) : u32x4{0, 0, 0, 0};
       qr[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // Flags, in one load per lane: lane 63 reads the unit's step t-1 stamp (the state
+  // of step t-1 must be complete), lanes below min(n_st, 63) the ready flags of the
+  // staged tiles. Tiles [0, ready_upto) are then known ready; later ones are checked
+  // when their copy is issued. One acquire covers everything observed.
+  const uint64_t* flags = a.slot_flags + (t & 1) * a.n_tiles;
+  const uint64_t st = stamp(a.epoch, t);
+  const int n_st = (kend + kStageRows - 1) / kStageRows;
+  int ready_upto;
+  {
+    const int nt0 = min(n_st, 63);
+    bool r = true;
+    if (lane < nt0) r = ld64(&flags[lane]) == st;
+    else if (lane == 63 && t > 0) r = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t - 1);
+    const uint64_t notready = __ballot(!r);
+    const uint64_t tiles_nr = notready & ~(1ull << 63);
+    ready_upto = (int)wave_bcast(tiles_nr ? (uint32_t)__builtin_ctzll(tiles_nr) : (uint32_t)nt0);
+    if ((notready >> 63) & 1) {
+      // The unit's previous step is still running: wait for it (acquires on return).
+      ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t - 1), waited);
+    } else {
+      fence_acquire();
     }
   }
 
@@ -908,12 +915,16 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     }
   }
   // Publish: unit step done (orders the state for step t+1) and slot release. Every
-  // wave's stores precede the barrier; one agent-scope release by thread 0 covers them.
+  // wave's stores precede the barrier; one agent-scope release fence by thread 0 covers
+  // them and both signals after it. (A wave whose wait failed has raised the launch's
+  // error; publishing after another workgroup's error is harmless, since every wait
+  // ends on it.)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  if (tid == 0 && !has_error(a)) {
-    st64_release(&a.unit_flags[unit], stamp(a.epoch, t));
-    __hip_atomic_fetch_add(&a.done_count[t], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && ok) {
+    fence_release();
+    __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&a.done_count[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1133,7 +1144,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
         add64(&a.ctrl->compute_ticks.v, busy);
         add32(&a.ctrl->compute_done.v, 1);
         add64(&a.ctrl->compute_wait_ticks.v, w0);
-        trace_rec(kernel_args(), kTraceCompute, x, y, (int64_t)t0, (int64_t)w0, 0, 0);
+        if (a.trace != nullptr) trace_rec(kernel_args(), kTraceCompute, x, y, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
       stage_tile<D>(a, kernel_args(), (uint32_t)x, y != 0);
