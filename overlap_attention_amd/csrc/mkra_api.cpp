@@ -333,7 +333,9 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   GROW(done_count, w->done_cap, n_steps, true);
   GROW(slot_flags, w->tiles_cap, 2 * (size_t)a.n_tiles, true);
   GROW(unit_flags, w->units_cap, n_units, true);
-  GROW(slots, w->slot_bytes_cap, 2 * (size_t)a.slot_bytes, false);
+  // The two ring slots, then one block of scratch that the compute role's discarded
+  // copies read (its contents are never used).
+  GROW(slots, w->slot_bytes_cap, 2 * (size_t)a.slot_bytes + mkra::kDiscardBytes, false);
   if (n_steps > 1) GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
   if (opts.trace) {
     size_t cap = (size_t)(opts.trace_capacity > 0 ? opts.trace_capacity : 262144);

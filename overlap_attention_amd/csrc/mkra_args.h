@@ -18,6 +18,9 @@ constexpr int kBN = 64;
 constexpr int kStageRows = 128;
 // LDS pipeline depth of the compute role: KV blocks in flight per workgroup.
 constexpr int kStages = 4;
+// Bytes after the two ring slots that the compute role's discarded block copies read
+// (one block of the largest head dim; the contents are never used).
+constexpr int kDiscardBytes = 2 * kBN * 128 * 2;
 constexpr int kMaxXcd = 8;
 
 // A staged KV block: the keys [64*kt, 64*kt + 64) of one KV head, laid out as the
@@ -135,7 +138,7 @@ struct KernelArgs {
   int64_t slot_bytes;     // Hkv * n_blocks * block bytes
 
   // Workspace (library-owned device memory).
-  uint8_t* slots;         // [2][Hkv][n_blocks] staged blocks
+  uint8_t* slots;         // [2][Hkv][n_blocks] staged blocks, then kDiscardBytes
   uint64_t* slot_flags;   // [2][n_tiles] epoch-stamped ready flags
   uint64_t* unit_flags;   // [n_units] epoch-stamped "step done" per unit
   float* acc;             // [n_units][kWaves][32*D + 256] running (O, m, l, lr) between steps

@@ -674,6 +674,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   // in SGPRs, per-lane offsets in VGPRs that the compiler may not recompute inside
   // the matrix phase).
   const uint8_t* const sblk_w = wave_bcast_ptr(sblk + w * 64 * 16);
+  // This wave's slice of the discard block (after both ring slots).
+  const uint8_t* const discard_w = wave_bcast_ptr(a.slots + 2 * a.slot_bytes + w * 64 * 16);
+  static_assert(Block<D>::kBytes <= kDiscardBytes, "discard block");
   CopyLanes<D> cl;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -798,9 +801,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
   // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
   // copy is block m+2 when it exists and its staged tile is known to be ready; else it
-  // copies a valid block (m+2 clamped) whose contents nobody reads, and block m+2, if
-  // it exists, is copied again after the MFMAs once its flag is seen (same wave, same
-  // LDS addresses, completes later). So every wait below has at least one block copy
+  // copies the discard block (one block after the ring slots, always cache-hot, never
+  // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
+  // is seen (same wave, same LDS addresses, completes later). So every wait below has at least one block copy
   // issued after the one it needs, and waiting until at most NI copy instructions are
   // outstanding is enough (it may also cover a discarded copy).
   auto wait_block = [&]() { wait_vm(NI); };
@@ -816,7 +819,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     // in SGPRs across the loop.
     uint32_t m0w = m0w_task;
     asm volatile("" : "+s"(m0w));
-    mfmas(sblk_w + (int64_t)min(kn, n_kt - 1) * Block<D>::kBytes, m0w);
+    mfmas(ready ? sblk_w + (int64_t)kn * Block<D>::kBytes : discard_w, m0w);
     pin_scores();
     pin_acc();
     if (kn < n_kt && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
@@ -836,7 +839,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   // unit's first query).
   issue(0, std::integral_constant<int, 0>{});
   if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
-  else dma_block<D, 1>(sblk_w, cl, m0w_task);  // discarded (see the copy rule above)
+  else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
   if (grp) {
     wait_block();
     __builtin_amdgcn_s_barrier();
