@@ -251,6 +251,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   a.lse = static_cast<float*>(lse->data);
   a.lq = (int)lq; a.lk = (int)lk; a.hq = (int)hq; a.hkv = (int)hkv; a.d = (int)d; a.gqa = gqa;
   a.n_chunks = n_chunks; a.rank = rank; a.causal = causal ? 1 : 0; a.n_steps = n_steps;
+  a.n_groups = (n_steps + mkra::kGroup - 1) / mkra::kGroup;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.hg = heads_per_unit(gqa);
   a.n_hgroups = gqa / a.hg;
@@ -331,11 +332,11 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     if ((e = hipMemsetAsync(w->status, 0, sizeof(DevStatus), stream)) != hipSuccess) return hip_fail(e, "memset");
   }
   GROW(done_count, w->done_cap, n_steps, true);
-  GROW(slot_flags, w->tiles_cap, 2 * (size_t)a.n_tiles, true);
+  GROW(slot_flags, w->tiles_cap, mkra::kSlots * (size_t)a.n_tiles, true);
   GROW(unit_flags, w->units_cap, n_units, true);
-  // The two ring slots, then one block of scratch that the compute role's discarded
-  // copies read (its contents are never used).
-  GROW(slots, w->slot_bytes_cap, 2 * (size_t)a.slot_bytes + mkra::kDiscardBytes, false);
+  // The ring slots, then one block of scratch that the compute role's discarded copies
+  // read (its contents are never used).
+  GROW(slots, w->slot_bytes_cap, mkra::kSlots * (size_t)a.slot_bytes + mkra::kDiscardBytes, false);
   if (n_steps > 1) GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
   if (opts.trace) {
     size_t cap = (size_t)(opts.trace_capacity > 0 ? opts.trace_capacity : 262144);

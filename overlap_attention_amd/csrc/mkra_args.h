@@ -18,7 +18,17 @@ constexpr int kBN = 64;
 constexpr int kStageRows = 128;
 // LDS pipeline depth of the compute role: KV blocks in flight per workgroup.
 constexpr int kStages = 4;
-// Bytes after the two ring slots that the compute role's discarded block copies read
+// Ring slots in HBM: step t is staged into slot t % kSlots, which is free once every
+// unit has finished step t - kSlots.
+constexpr int kSlots = 4;
+// Ring steps per compute task: a task runs kGroup consecutive steps of one unit with
+// the running state in registers, so the state is stored and reloaded, and a task
+// claimed, once per kGroup steps. A task of group g needs steps kGroup*g .. staged,
+// which needs every unit past step kGroup*g + kGroup - 1 - kSlots, i.e. group g-2
+// complete when kSlots = 2*kGroup: one group of claim look-ahead stays deadlock-free.
+constexpr int kGroup = 2;
+static_assert(kSlots >= 2 * kGroup, "a group task may depend only on groups <= g-2");
+// Bytes after the ring slots that the compute role's discarded block copies read
 // (one block of the largest head dim; the contents are never used).
 constexpr int kDiscardBytes = 2 * kBN * 128 * 2;
 constexpr int kMaxXcd = 8;
@@ -117,6 +127,7 @@ struct KernelArgs {
   float* lse;             // [Hq, Lq] fp32
   int lq, lk, hq, hkv, d, gqa;
   int n_chunks, rank, causal, n_steps;
+  int n_groups;           // ceil(n_steps / kGroup): compute tasks per unit
   float scale_log2;       // log2(e) / sqrt(D)
 
   // Decomposition into compute units: a unit is (KV head, group of HG query heads
@@ -138,8 +149,8 @@ struct KernelArgs {
   int64_t slot_bytes;     // Hkv * n_blocks * block bytes
 
   // Workspace (library-owned device memory).
-  uint8_t* slots;         // [2][Hkv][n_blocks] staged blocks, then kDiscardBytes
-  uint64_t* slot_flags;   // [2][n_tiles] epoch-stamped ready flags
+  uint8_t* slots;         // [kSlots][Hkv][n_blocks] staged blocks, then kDiscardBytes
+  uint64_t* slot_flags;   // [kSlots][n_tiles] epoch-stamped ready flags
   uint64_t* unit_flags;   // [n_units] epoch-stamped "step done" per unit
   float* acc;             // [n_units][kWaves][32*D + 256] running (O, m, l, lr) between steps
   uint32_t* done_count;   // [n_steps] units finished per step (slot release)

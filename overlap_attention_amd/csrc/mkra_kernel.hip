@@ -161,7 +161,18 @@ __device__ __forceinline__ int64_t units_in_queue(const KA& a, int x) {
   return a.xcd_unit_begin[x + 1] - a.xcd_unit_begin[x];
 }
 
-// Run by one lane, from a snapshot of the queue heads and the staging head.
+// Unit-steps covered by the first h tasks of a queue of ux units (tasks are
+// group-major; every group has kGroup steps but possibly the last).
+template <class KA>
+__device__ __forceinline__ int64_t steps_claimed(const KA& a, int64_t ux, int64_t h) {
+  if (h >= ux * a.n_groups) return ux * a.n_steps;
+  const int64_t g = h / ux;
+  const int64_t in_g = min((int64_t)kGroup, (int64_t)a.n_steps - g * kGroup);
+  return ux * g * kGroup + (h % ux) * in_g;
+}
+
+// Run by one lane, from a snapshot of the queue heads and the staging head. Compute
+// work is counted in unit-steps (R_p remaining, C_p measured per unit-step).
 // Rate-limited by a compare-and-swap on the update time.
 __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uint32_t (&heads)[kMaxXcd],
                                                  uint32_t stage_head, uint64_t last) {
@@ -175,8 +186,7 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
 #pragma unroll
   for (int x = 0; x < kMaxXcd; ++x) {
     if (x >= a.n_xcd) break;
-    int64_t tot = units_in_queue(a, x) * a.n_steps;
-    claimed += (int64_t)heads[x] < tot ? (int64_t)heads[x] : tot;
+    claimed += steps_claimed(a, units_in_queue(a, x), (int64_t)heads[x]);
   }
   int64_t rp = (int64_t)a.n_units * a.n_steps - claimed;
   uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
@@ -319,8 +329,9 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // One staging task, run by the whole workgroup: 128-row tile j of the chunk of step
 // t (chunk (rank - t) mod N, read from its home in kv_chunks, which stands for the
-// predecessor's memory) becomes staged blocks in slot t % 2: K swizzled, V transposed
-// to fp16. The slot is free once every unit has finished step t - 2. One release per
+// predecessor's memory) becomes staged blocks in slot t % kSlots: K swizzled, V
+// transposed to fp16. The slot is free once every unit has finished step t - kSlots.
+// One release per
 // tile publishes its epoch-stamped flag (paper §4: epoch-stamped readiness flags).
 template <int D>
 __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k, bool assist) {
@@ -333,10 +344,10 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
   const uint64_t t_begin = ticks();
   const int t = (int)k / a.n_tiles;
   const int j = (int)k % a.n_tiles;
-  const int slot = t & 1;
+  const int slot = t % kSlots;
   uint64_t w = 0;
   // Slot release (every wave waits; a timeout leaves the error word set for all).
-  if (t >= 2) wave_wait_ge32(a, &a.done_count[t - 2], (uint32_t)a.n_units, w);
+  if (t >= kSlots) wave_wait_ge32(a, &a.done_count[t - kSlots], (uint32_t)a.n_units, w);
   __syncthreads();
   const bool ok = !has_error(a);
   __syncthreads();
@@ -572,7 +583,7 @@ struct MPhase {
 };
 
 template <int D>
-__device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint64_t& waited) {
+__device__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int NI = Block<D>::kChunksPerThread;  // block-copy instructions per wave per tile
@@ -582,18 +593,17 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
   // The task comes through LDS; telling the compiler it is uniform keeps every
   // address derived from it (slot, head, block) in SGPRs.
   unit = (int)wave_bcast((uint32_t)unit);
-  t = (int)wave_bcast((uint32_t)t);
+  step_group = (int)wave_bcast((uint32_t)step_group);
+  // The task's ring steps: [t_first, t_end), with the running state in registers
+  // from one step to the next.
+  const int t_first = step_group * kGroup, t_end = min(a.n_steps, t_first + kGroup);
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
   const int kvh = p / a.n_hgroups, hgi = p % a.n_hgroups;
   const int h = kvh * a.gqa + hgi * a.hg + (w % a.hg);
   const int q0w = qb * a.bq + (w / a.hg) * kRowsPerWave;
   const bool wave_rows = q0w < a.lq;
   const int qrow = q0w + col;
-  const bool diag = a.causal && t == 0;
-  const uint8_t* sblk = a.slots + (int64_t)(t & 1) * a.slot_bytes + (int64_t)kvh * a.n_blocks * Block<D>::kBytes;
   const int q_end = min(a.lq, qb * a.bq + a.bq);
-  const int kend = diag ? min(a.lk, q_end) : a.lk;
-  const int n_kt = (kend + kBN - 1) / kBN;
   const float c2 = a.scale_log2;
   bool ok = true;
 
@@ -610,36 +620,66 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     }
   }
 
-  // Flags, in one load per lane: lane 63 reads the unit's step t-1 stamp (the state
-  // of step t-1 must be complete), lanes below min(n_st, 63) the ready flags of the
-  // staged tiles. Tiles [0, ready_upto) are then known ready; later ones are checked
-  // when their copy is issued. One acquire covers everything observed.
-  const uint64_t* flags = a.slot_flags + (t & 1) * a.n_tiles;
-  const uint64_t st = stamp(a.epoch, t);
-  const int n_st = (kend + kStageRows - 1) / kStageRows;
-  int ready_upto;
+  // Running state: Oᵀ blocks, max (log2 units of the scaled score) and the running sum
+  // of P.
+  f32x16 o[DB];
+  float m_run, l_run;
+  float* accw = a.acc + ((int64_t)unit * kWaves + w) * (32 * D + 256);
+  // Per-lane LDS addresses (the swizzles depend only on the lane).
+  LaneAddr<D> la;
   {
-    const int nt0 = min(n_st, 63);
+    const uint32_t b0 = lds_base();
+    const int kx = (D == 128) ? (col & 15) : ((col >> 1) & 7);
+    const int vx = (col >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) la.k[kk] = b0 + col * (D * 2) + 16 * ((2 * kk + hi) ^ kx);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) la.v[pp] = b0 + stage_v<D, 0>() + col * 128 + 16 * ((2 * pp + hi) ^ vx);
+  }
+
+  // Copy addressing: this wave's 1 KB slice of every copy instruction (base in SGPRs,
+  // per-lane offsets in VGPRs that the compiler may not recompute inside the matrix
+  // phase). The discard block follows the ring slots.
+  const uint8_t* const discard_w = wave_bcast_ptr(a.slots + kSlots * a.slot_bytes + w * 64 * 16);
+  static_assert(Block<D>::kBytes <= kDiscardBytes, "discard block");
+  CopyLanes<D> cl;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    cl.off[i] = (uint32_t)(i * kThreads * 16 + lane * 16);
+    asm volatile("" : "+v"(cl.off[i]));
+  }
+  const uint32_t m0w_task = lds_base() + (uint32_t)w * 64u * 16u;
+  // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
+  f32x16 s[kBN / 32];
+  f16x8 pb[kBN / 16];
+
+  // Flags of step t, in one load per lane: lanes below min(n_st, 63) read the ready
+  // flags of the staged tiles and, when unit_flag is set, lane 63 the unit's step t-1
+  // stamp (the state of step t-1 must be complete). Tiles [0, returned value) are then
+  // known ready; later ones are checked when their copy is issued. One acquire covers
+  // everything observed.
+  auto kend_of = [&](int t) { return (a.causal && t == 0) ? min(a.lk, q_end) : a.lk; };
+  auto check_flags = [&](int t, bool unit_flag) -> int {
+    const uint64_t* flags = a.slot_flags + (t % kSlots) * a.n_tiles;
+    const uint64_t st = stamp(a.epoch, t);
+    const int nt0 = min((kend_of(t) + kStageRows - 1) / kStageRows, 63);
     bool r = true;
     if (lane < nt0) r = ld64(&flags[lane]) == st;
-    else if (lane == 63 && t > 0) r = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t - 1);
+    else if (lane == 63 && unit_flag) r = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t - 1);
     const uint64_t notready = __ballot(!r);
     const uint64_t tiles_nr = notready & ~(1ull << 63);
-    ready_upto = (int)wave_bcast(tiles_nr ? (uint32_t)__builtin_ctzll(tiles_nr) : (uint32_t)nt0);
+    const int upto = (int)wave_bcast(tiles_nr ? (uint32_t)__builtin_ctzll(tiles_nr) : (uint32_t)nt0);
     if ((notready >> 63) & 1) {
       // The unit's previous step is still running: wait for it (acquires on return).
       ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t - 1), waited);
     } else {
       fence_acquire();
     }
-  }
+    return upto;
+  };
+  const int ready_first = check_flags(t_first, t_first > 0);
 
-  // Running state: Oᵀ blocks, max (log2 units of the scaled score) and the running sum
-  // of P.
-  f32x16 o[DB];
-  float m_run, l_run;
-  float* accw = a.acc + ((int64_t)unit * kWaves + w) * (32 * D + 256);
-  if (t == 0) {
+  if (t_first == 0) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     m_run = -INFINITY;
@@ -658,236 +698,221 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
     l_run = ml[1];
   }
 
-  // Per-lane LDS addresses (the swizzles depend only on the lane).
-  LaneAddr<D> la;
-  {
-    const uint32_t b0 = lds_base();
-    const int kx = (D == 128) ? (col & 15) : ((col >> 1) & 7);
-    const int vx = (col >> 1) & 7;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) la.k[kk] = b0 + col * (D * 2) + 16 * ((2 * kk + hi) ^ kx);
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) la.v[pp] = b0 + stage_v<D, 0>() + col * 128 + 16 * ((2 * pp + hi) ^ vx);
-  }
+  for (int t = t_first; t < t_end; ++t) {
+    const bool diag = a.causal && t == 0;
+    const uint8_t* sblk =
+        a.slots + (int64_t)(t % kSlots) * a.slot_bytes + (int64_t)kvh * a.n_blocks * Block<D>::kBytes;
+    const int kend = kend_of(t);
+    const int n_kt = (kend + kBN - 1) / kBN;
+    const uint8_t* const sblk_w = wave_bcast_ptr(sblk + w * 64 * 16);
+    const uint64_t* flags = a.slot_flags + (t % kSlots) * a.n_tiles;
+    const uint64_t st = stamp(a.epoch, t);
+    const int n_st = (kend + kStageRows - 1) / kStageRows;
+    int ready_upto = t == t_first ? ready_first : check_flags(t, false);
 
-  // Per-task copy addressing: this wave's 1 KB slice of every copy instruction (base
-  // in SGPRs, per-lane offsets in VGPRs that the compiler may not recompute inside
-  // the matrix phase).
-  const uint8_t* const sblk_w = wave_bcast_ptr(sblk + w * 64 * 16);
-  // This wave's slice of the discard block (after both ring slots).
-  const uint8_t* const discard_w = wave_bcast_ptr(a.slots + 2 * a.slot_bytes + w * 64 * 16);
-  static_assert(Block<D>::kBytes <= kDiscardBytes, "discard block");
-  CopyLanes<D> cl;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    cl.off[i] = (uint32_t)(i * kThreads * 16 + lane * 16);
-    asm volatile("" : "+v"(cl.off[i]));
-  }
-  const uint32_t m0w_task = lds_base() + (uint32_t)w * 64u * 16u;
-  auto issue = [&](int kt, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    const int j = (kt * kBN) / kStageRows;
-    if (j >= ready_upto) {
-      // Wait for this tile's flag, then look at all later flags at once (one load per
-      // lane) so the next few tiles need no check.
-      ok &= wave_wait_stamp(a, &flags[j], st, waited);
-      int upto = j + 1;
-      for (int j0 = j + 1; j0 < n_st; j0 += 64) {
-        const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
-        const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
-        if (notready) {
-          upto = j0 + (int)__builtin_ctzll(notready);
-          break;
+    auto issue = [&](int kt, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int j = (kt * kBN) / kStageRows;
+      if (j >= ready_upto) {
+        // Wait for this tile's flag, then look at all later flags at once (one load per
+        // lane) so the next few tiles need no check.
+        ok &= wave_wait_stamp(a, &flags[j], st, waited);
+        int upto = j + 1;
+        for (int j0 = j + 1; j0 < n_st; j0 += 64) {
+          const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
+          const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
+          if (notready) {
+            upto = j0 + (int)__builtin_ctzll(notready);
+            break;
+          }
+          upto = min(n_st, j0 + 64);
         }
-        upto = min(n_st, j0 + 64);
+        if (upto > j + 1) fence_acquire();
+        ready_upto = (int)wave_bcast((uint32_t)upto);
       }
-      if (upto > j + 1) fence_acquire();
-      ready_upto = (int)wave_bcast((uint32_t)upto);
-    }
-    dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, cl, m0w_task);
-  };
-
-  // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
-  f32x16 s[kBN / 32];
-  f16x8 pb[kBN / 16];
-
-  // Online-softmax update for block kt (FlashAttention-2), producing fp16 Pᵀ.
-  auto softmax = [&](int kt) {
-    // Masks: ragged key tail, and keys after the query on the diagonal step.
-    const int k0 = kt * kBN;
-    if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
-      // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
-      // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
-      const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
-    }
-    // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
-    // fp32 P (four partial sums, short dependency chains) and the PV product takes P
-    // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
-    // the rounded P would not co-issue with the other wave's MFMAs.)
-    float lsum;
-    auto exp_block = [&](float mref) {
-      float ls[4];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-          ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
-          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
-        }
-      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, cl, m0w_task);
     };
-    exp_block(m_run);
-    // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
-    // of its P), or on the first block, is the row max of the block needed: raise
-    // m_run to it, rescale O and l, and redo the block. The max the exponentials use
-    // may therefore lag the true max, by at most log2(kSumMax); every P stays in the
-    // fp16 range and the algebra of the online softmax is unchanged.
-    if (__any(!(lsum <= kSumMax))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float alpha = (m_new == m_run || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
-                                                                 : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-      exp_block(m_run == -INFINITY ? 0.f : m_run);
-    }
-    l_run += lsum;
-  };
 
-  // Two-phase schedule. Each wave runs M(0) V(0) M(1) V(1) ... M(n_kt), where
-  // M(m) = PV of block m-1 and QKᵀ of block m (matrix cores) and V(m) = the softmax
-  // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
-  // one extra barrier first and group 0 one at the end, so the two waves sharing a
-  // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
-  // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
-  // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
-  // both groups pass only once they are done with it. Before every barrier a wave
-  // waits for its own copies of the next block it or the other group reads; the
-  // barrier then makes every wave's part visible.
-  // Every wave runs every block of the unit: on the diagonal step the blocks past a
-  // wave's last query are fully masked and add exactly zero.
-  //
-  // The compiler may move register-only arithmetic across s_barrier (it orders only
-  // memory), which would pull softmax work into the matrix phase or the reverse and
-  // undo the ping-pong. Empty volatile asm statements, which keep their order with
-  // the barriers, pin each phase's inputs after its barrier and its outputs before
-  // the next one.
-  auto pin_scores = [&]() {
-    if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
-  };
-  auto pin_acc = [&]() {
-    if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
-    else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
-  };
-  auto pin_state = [&]() {
-    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
-    pin_acc();
-  };
-  // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
-  // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
-  // copy is block m+2 when it exists and its staged tile is known to be ready; else it
-  // copies the discard block (one block after the ring slots, always cache-hot, never
-  // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
-  // is seen (same wave, same LDS addresses, completes later). So every wait below has at least one block copy
-  // issued after the one it needs, and waiting until at most NI copy instructions are
-  // outstanding is enough (it may also cover a discarded copy).
-  auto wait_block = [&]() { wait_vm(NI); };
-  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
-  auto mstep = [&](int m, auto stage_tag, auto mfmas) {
-    constexpr int S = decltype(stage_tag)::value;
-    if (m < n_kt) wait_block();
-    __builtin_amdgcn_s_barrier();
-    const int kn = m + 2;
-    const bool ready = wave_bcast(kn < n_kt && (kn * kBN) / kStageRows < ready_upto) != 0;
-    // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
-    // and instruction offsets here (scalar adds) instead of keeping sixteen of them
-    // in SGPRs across the loop.
-    uint32_t m0w = m0w_task;
-    asm volatile("" : "+s"(m0w));
-    mfmas(ready ? sblk_w + (int64_t)kn * Block<D>::kBytes : discard_w, m0w);
-    pin_scores();
-    pin_acc();
-    if (kn < n_kt && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
-  };
-  auto vstep = [&](int m) {
-    if (m + 1 < n_kt) wait_block();
-    __builtin_amdgcn_s_barrier();
-    pin_scores();
-    softmax(m);
-    pin_state();
-  };
+    // Online-softmax update for block kt (FlashAttention-2), producing fp16 Pᵀ.
+    auto softmax = [&](int kt) {
+      // Masks: ragged key tail, and keys after the query on the diagonal step.
+      const int k0 = kt * kBN;
+      if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
+        // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
+        // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
+        const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
+      }
+      // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
+      // fp32 P (four partial sums, short dependency chains) and the PV product takes P
+      // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
+      // the rounded P would not co-issue with the other wave's MFMAs.)
+      float lsum;
+      auto exp_block = [&](float mref) {
+        float ls[4];
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
+            ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
+            pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
+          }
+        lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      exp_block(m_run);
+      // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
+      // of its P), or on the first block, is the row max of the block needed: raise
+      // m_run to it, rescale O and l, and redo the block. The max the exponentials use
+      // may therefore lag the true max, by at most log2(kSumMax); every P stays in the
+      // fp16 range and the algebra of the online softmax is unchanged.
+      if (__any(!(lsum <= kSumMax))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * c2);
+        const float alpha = (m_new == m_run || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
+                                                                   : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+        exp_block(m_run == -INFINITY ? 0.f : m_run);
+      }
+      l_run += lsum;
+    };
+
+    // Two-phase schedule. Each wave runs M(0) V(0) M(1) V(1) ... M(n_kt), where
+    // M(m) = PV of block m-1 and QKᵀ of block m (matrix cores) and V(m) = the softmax
+    // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
+    // one extra barrier first and group 0 one at the end, so the two waves sharing a
+    // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
+    // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
+    // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
+    // both groups pass only once they are done with it. Before every barrier a wave
+    // waits for its own copies of the next block it or the other group reads; the
+    // barrier then makes every wave's part visible.
+    // Every wave runs every block of the unit: on the diagonal step the blocks past a
+    // wave's last query are fully masked and add exactly zero.
+    //
+    // The compiler may move register-only arithmetic across s_barrier (it orders only
+    // memory), which would pull softmax work into the matrix phase or the reverse and
+    // undo the ping-pong. Empty volatile asm statements, which keep their order with
+    // the barriers, pin each phase's inputs after its barrier and its outputs before
+    // the next one.
+    auto pin_scores = [&]() {
+      if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    };
+    auto pin_acc = [&]() {
+      if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+      else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
+    };
+    auto pin_state = [&]() {
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
+      pin_acc();
+    };
+    // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
+    // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
+    // copy is block m+2 when it exists and its staged tile is known to be ready; else it
+    // copies the discard block (one block after the ring slots, always cache-hot, never
+    // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
+    // is seen (same wave, same LDS addresses, completes later). So every wait below has at least one block copy
+    // issued after the one it needs, and waiting until at most NI copy instructions are
+    // outstanding is enough (it may also cover a discarded copy).
+    auto wait_block = [&]() { wait_vm(NI); };
+    // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
+    auto mstep = [&](int m, auto stage_tag, auto mfmas) {
+      constexpr int S = decltype(stage_tag)::value;
+      if (m < n_kt) wait_block();
+      __builtin_amdgcn_s_barrier();
+      const int kn = m + 2;
+      const bool ready = wave_bcast(kn < n_kt && (kn * kBN) / kStageRows < ready_upto) != 0;
+      // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
+      // and instruction offsets here (scalar adds) instead of keeping sixteen of them
+      // in SGPRs across the loop.
+      uint32_t m0w = m0w_task;
+      asm volatile("" : "+s"(m0w));
+      mfmas(ready ? sblk_w + (int64_t)kn * Block<D>::kBytes : discard_w, m0w);
+      pin_scores();
+      pin_acc();
+      if (kn < n_kt && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
+    };
+    auto vstep = [&](int m) {
+      if (m + 1 < n_kt) wait_block();
+      __builtin_amdgcn_s_barrier();
+      pin_scores();
+      softmax(m);
+      pin_state();
+    };
 #define MKRA_PVQK(S) \
-  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
+    [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
 #define MKRA_PV(S) \
-  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
-  // n_kt >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
-  // unit's first query).
-  issue(0, std::integral_constant<int, 0>{});
-  if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
-  else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
-  if (grp) {
-    wait_block();
-    __builtin_amdgcn_s_barrier();
-  }
-  mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
-    MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
-  });
-  vstep(0);
-  int m = 1;
-  for (; m + 3 < n_kt; m += kStages) {
-    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
-    vstep(m);
-    mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
-    vstep(m + 1);
-    mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
-    vstep(m + 2);
-    mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
-    vstep(m + 3);
-  }
-  if (m < n_kt) {
-    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
-    vstep(m);
-    if (++m < n_kt) {
-      mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+    [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
+    // n_kt >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
+    // unit's first query).
+    issue(0, std::integral_constant<int, 0>{});
+    if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
+    else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
+    if (grp) {
+      wait_block();
+      __builtin_amdgcn_s_barrier();
+    }
+    mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
+      MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
+    });
+    vstep(0);
+    int m = 1;
+    for (; m + 3 < n_kt; m += kStages) {
+      mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+      vstep(m);
+      mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+      vstep(m + 1);
+      mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+      vstep(m + 2);
+      mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
+      vstep(m + 3);
+    }
+    if (m < n_kt) {
+      mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
       vstep(m);
       if (++m < n_kt) {
-        mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+        mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
         vstep(m);
-        ++m;
+        if (++m < n_kt) {
+          mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+          vstep(m);
+          ++m;
+        }
       }
     }
-  }
-  // M(n_kt): PV of the last block only; no wait follows, so it copies nothing.
-  switch (n_kt & 3) {
-    case 0: mstep(n_kt, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
-    case 1: mstep(n_kt, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
-    case 2: mstep(n_kt, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
-    default: mstep(n_kt, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
-  }
+    // M(n_kt): PV of the last block only; no wait follows, so it copies nothing.
+    switch (n_kt & 3) {
+      case 0: mstep(n_kt, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
+      case 1: mstep(n_kt, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
+      case 2: mstep(n_kt, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
+      default: mstep(n_kt, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
+    }
 #undef MKRA_PVQK
 #undef MKRA_PV
-  if (!grp) __builtin_amdgcn_s_barrier();
-  // Discarded copies may still be in flight: drain them before this workgroup's next
-  // task (or staging task) writes the same LDS.
-  wait_vm(0);
+    if (!grp) __builtin_amdgcn_s_barrier();
+    // Discarded copies may still be in flight: drain them before this workgroup's next
+    // step, task or staging task writes the same LDS; the barrier keeps the next step's
+    // first copies out of stages that the other group may still be reading.
+    wait_vm(0);
+    if (t + 1 < t_end) __syncthreads();
+  }
 
   if (ok && wave_rows) {
-    if (t == a.n_steps - 1) {
+    if (t_end == a.n_steps) {
       // Finalise: out = O / l, lse = ln(2) * (m + log2 l).
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       if (qrow < a.lq) {
@@ -917,17 +942,18 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
       reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, 0.f, 0.f};
     }
   }
-  // Publish: unit step done (orders the state for step t+1) and slot release. Every
-  // wave's stores precede the barrier; one agent-scope release fence by thread 0 covers
-  // them and both signals after it. (A wave whose wait failed has raised the launch's
-  // error; publishing after another workgroup's error is harmless, since every wait
-  // ends on it.)
+  // Publish: unit steps done (orders the state for the next group) and slot release for
+  // each step of the task. Every wave's stores precede the barrier; one agent-scope
+  // release fence by thread 0 covers them and every signal after it. (A wave whose
+  // wait failed has raised the launch's error; publishing after another workgroup's
+  // error is harmless, since every wait ends on it.)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0 && ok) {
     fence_release();
-    __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&a.done_count[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t_end - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = t_first; t < t_end; ++t)
+      __hip_atomic_fetch_add(&a.done_count[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -937,7 +963,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int t, int grp, uint
 struct Sched {
   int32_t role;     // kRoleCompute / kRoleStage
   int32_t pending;  // a claimed compute task not yet run
-  int32_t pend_u, pend_t;
+  int32_t pend_u, pend_g;  // the pending task: unit and step group
 };
 
 // Picks the workgroup's next task and writes (op, x, y) to cmd. Run by thread 0.
@@ -946,19 +972,22 @@ struct Sched {
 // round trip plus, for a compute task, one compare-and-swap (these words are shared
 // by all XCDs, so each access goes to memory).
 //
-// Compute tasks: each XCD has a queue of the units of its head groups, step-major, so
-// units that read the same KV head share an L2. A workgroup takes from its own queue
-// only while that queue is at most one step ahead of the slowest queue, else from the
-// slowest queue: every claimed task then needs only staging of steps whose slot
-// release depends on tasks already claimed, so the schedule cannot deadlock whatever
-// subset of workgroups is resident. Within a step a queue runs its units from the
-// last, so on the causal diagonal step the longest query blocks start first.
+// Compute tasks: a task is one unit for kGroup consecutive ring steps (a step group).
+// Each XCD has a queue of the units of its head groups, group-major, so units that
+// read the same KV head share an L2. A workgroup takes from its own queue only while
+// that queue is at most one group ahead of the slowest queue, else from the slowest
+// queue. A task of group g needs its unit's group g-1 (claimed earlier, same queue
+// order) and staging of its steps, whose slots are released once group g-2 is complete
+// (kSlots = 2 kGroup); every task of group g-2 is claimed when the rule admits group
+// g, so the schedule cannot deadlock whatever subset of workgroups is resident. Within
+// a group a queue runs its units from the last, so on the causal diagonal step the
+// longest query blocks start first.
 //
 // Roles change at task boundaries (§3.2): a staging workgroup leaves the role when
 // staging is done or the controller's target dropped below the count; a compute
 // workgroup joins when the count is below the target. The stall rule of §3.2: while
 // staging work that a claimed compute task depends on is unclaimed (tasks of steps up
-// to its own whose slot is already released), the workgroup does that work first.
+// to its last whose slot is already released), the workgroup does that work first.
 __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_t* cmd) {
   const KernelArgs& a = *ap;
   // Wave 0 loads the control words lane-parallel (one instruction, one round trip);
@@ -1024,25 +1053,25 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
       const int own = (int)(blockIdx.x % (unsigned)a.n_xcd);
       bool got = false;
       for (int attempt = 0; attempt < 1 << 16 && !got; ++attempt) {
-        int min_step = a.n_steps, min_x = -1, own_step = a.n_steps;
+        int min_step = a.n_groups, min_x = -1, own_step = a.n_groups;
         uint32_t own_head = 0, min_head = 0;
 #pragma unroll
         for (int q = 0; q < kMaxXcd; ++q) {
           if (q >= a.n_xcd) break;
           const int64_t ux = units_in_queue(a, q);
-          const int sq = (ux == 0 || (int64_t)heads[q] >= ux * a.n_steps) ? a.n_steps : (int)(heads[q] / ux);
+          const int sq = (ux == 0 || (int64_t)heads[q] >= ux * a.n_groups) ? a.n_groups : (int)(heads[q] / ux);
           if (q == own) { own_step = sq; own_head = heads[q]; }
           if (sq < min_step) { min_step = sq; min_x = q; min_head = heads[q]; }
         }
         if (min_x < 0) break;  // every queue exhausted
-        const bool mine = own_step < a.n_steps && own_step <= min_step + 1;
+        const bool mine = own_step < a.n_groups && own_step <= min_step + 1;
         const int q = mine ? own : min_x;
         const uint32_t h = mine ? own_head : min_head;
         uint32_t expect = h;
         if (__hip_atomic_compare_exchange_strong(&a.ctrl->xcd_head[q].v, &expect, h + 1, __ATOMIC_RELAXED,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           const int64_t ux = units_in_queue(a, q);
-          st->pend_t = (int32_t)(h / ux);
+          st->pend_g = (int32_t)(h / ux);
           st->pend_u = a.xcd_unit_begin[q + 1] - 1 - (int32_t)(h % ux);
           got = true;
         } else {
@@ -1070,11 +1099,12 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     uint32_t h = sh;
     bool assist = false;
     int released_below = 0;  // steps whose slot is known released
+    const int pend_last = min(a.n_steps, (st->pend_g + 1) * kGroup) - 1;  // last step the task runs
     for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
       const int step = (int)h / a.n_tiles;
-      if (step > st->pend_t) break;
-      if (step >= 2 && step >= released_below) {
-        if (ld32(&a.done_count[step - 2]) < (uint32_t)a.n_units) break;
+      if (step > pend_last) break;
+      if (step >= kSlots && step >= released_below) {
+        if (ld32(&a.done_count[step - kSlots]) < (uint32_t)a.n_units) break;
         released_below = step + 1;
       }
       uint32_t expect = h;
@@ -1092,7 +1122,7 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     } else {
       op = kOpCompute;
       x = st->pend_u;
-      y = st->pend_t;
+      y = st->pend_g;
       st->pending = 0;
     }
   }
@@ -1144,10 +1174,13 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       compute_task<D>(a, x, y, grp, w0);
       if (tid == 0) {
         const uint64_t busy = ticks() - t0 - w0;
+        const int t_first = y * kGroup, t_end = min(a.n_steps, t_first + kGroup);
         add64(&a.ctrl->compute_ticks.v, busy);
-        add32(&a.ctrl->compute_done.v, 1);
+        add32(&a.ctrl->compute_done.v, (uint32_t)(t_end - t_first));  // unit-steps
         add64(&a.ctrl->compute_wait_ticks.v, w0);
-        if (a.trace != nullptr) trace_rec(kernel_args(), kTraceCompute, x, y, (int64_t)t0, (int64_t)w0, 0, 0);
+        if (a.trace != nullptr)
+          for (int t = t_first; t < t_end; ++t)
+            trace_rec(kernel_args(), kTraceCompute, x, t, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
       stage_tile<D>(a, kernel_args(), (uint32_t)x, y != 0);
