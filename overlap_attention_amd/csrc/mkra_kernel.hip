@@ -653,31 +653,45 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   f32x16 s[kBN / 32];
   f16x8 pb[kBN / 16];
 
-  // Flags of step t, in one load per lane: lanes below min(n_st, 63) read the ready
-  // flags of the staged tiles and, when unit_flag is set, lane 63 the unit's step t-1
-  // stamp (the state of step t-1 must be complete). Tiles [0, returned value) are then
-  // known ready; later ones are checked when their copy is issued. One acquire covers
-  // everything observed.
+  // The task's KV blocks form one sequence: the n0 blocks of step t_first, then those
+  // of step t_first + 1 (kGroup = 2). The online softmax does not depend on where one
+  // step ends, so one pipeline runs through both steps without draining in between.
+  static_assert(kGroup == 2, "the block sequence covers two steps");
   auto kend_of = [&](int t) { return (a.causal && t == 0) ? min(a.lk, q_end) : a.lk; };
-  auto check_flags = [&](int t, bool unit_flag) -> int {
-    const uint64_t* flags = a.slot_flags + (t % kSlots) * a.n_tiles;
-    const uint64_t st = stamp(a.epoch, t);
-    const int nt0 = min((kend_of(t) + kStageRows - 1) / kStageRows, 63);
-    bool r = true;
-    if (lane < nt0) r = ld64(&flags[lane]) == st;
-    else if (lane == 63 && unit_flag) r = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t - 1);
-    const uint64_t notready = __ballot(!r);
-    const uint64_t tiles_nr = notready & ~(1ull << 63);
-    const int upto = (int)wave_bcast(tiles_nr ? (uint32_t)__builtin_ctzll(tiles_nr) : (uint32_t)nt0);
-    if ((notready >> 63) & 1) {
+  auto n_tiles_of = [&](int t) { return (kend_of(t) + kStageRows - 1) / kStageRows; };
+  const bool two = t_end - t_first > 1;
+  const int n0 = (kend_of(t_first) + kBN - 1) / kBN;
+  const int nb = n0 + (two ? (kend_of(t_first + 1) + kBN - 1) / kBN : 0);
+  const int64_t head_off = (int64_t)kvh * a.n_blocks * Block<D>::kBytes + w * 64 * 16;
+  const uint8_t* const sblk_w0 = wave_bcast_ptr(a.slots + (int64_t)(t_first % kSlots) * a.slot_bytes + head_off);
+  const uint8_t* const sblk_w1 =
+      wave_bcast_ptr(a.slots + (int64_t)((t_first + 1) % kSlots) * a.slot_bytes + head_off);
+  auto flags_of = [&](int t) { return a.slot_flags + (t % kSlots) * a.n_tiles; };
+
+  // Flags, in two loads per lane issued together (one round trip): lanes below
+  // min(n_st0, 63) read the ready flags of the staged tiles of step t_first and lane 63
+  // the unit's step t_first-1 stamp (that state must be complete); lanes below
+  // min(n_st1, 64) read those of step t_first+1. Tiles below ru0 (ru1) are then known
+  // ready; later ones are checked when their copy is issued. One acquire covers
+  // everything observed.
+  int ru0, ru1;
+  {
+    const int nt0 = min(n_tiles_of(t_first), 63), nt1 = two ? min(n_tiles_of(t_first + 1), 64) : 0;
+    bool r0 = true, r1 = true;
+    if (lane < nt0) r0 = ld64(&flags_of(t_first)[lane]) == stamp(a.epoch, t_first);
+    else if (lane == 63 && t_first > 0) r0 = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t_first - 1);
+    if (lane < nt1) r1 = ld64(&flags_of(t_first + 1)[lane]) == stamp(a.epoch, t_first + 1);
+    const uint64_t nr0 = __ballot(!r0), nr1 = __ballot(!r1);
+    const uint64_t tiles_nr0 = nr0 & ~(1ull << 63);
+    ru0 = (int)wave_bcast(tiles_nr0 ? (uint32_t)__builtin_ctzll(tiles_nr0) : (uint32_t)nt0);
+    ru1 = (int)wave_bcast(nr1 ? (uint32_t)__builtin_ctzll(nr1) : (uint32_t)nt1);
+    if ((nr0 >> 63) & 1) {
       // The unit's previous step is still running: wait for it (acquires on return).
-      ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t - 1), waited);
+      ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t_first - 1), waited);
     } else {
       fence_acquire();
     }
-    return upto;
-  };
-  const int ready_first = check_flags(t_first, t_first > 0);
+  }
 
   if (t_first == 0) {
 #pragma unroll
@@ -698,218 +712,223 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     l_run = ml[1];
   }
 
-  for (int t = t_first; t < t_end; ++t) {
-    const bool diag = a.causal && t == 0;
-    const uint8_t* sblk =
-        a.slots + (int64_t)(t % kSlots) * a.slot_bytes + (int64_t)kvh * a.n_blocks * Block<D>::kBytes;
-    const int kend = kend_of(t);
-    const int n_kt = (kend + kBN - 1) / kBN;
-    const uint8_t* const sblk_w = wave_bcast_ptr(sblk + w * 64 * 16);
-    const uint64_t* flags = a.slot_flags + (t % kSlots) * a.n_tiles;
-    const uint64_t st = stamp(a.epoch, t);
-    const int n_st = (kend + kStageRows - 1) / kStageRows;
-    int ready_upto = t == t_first ? ready_first : check_flags(t, false);
-
-    auto issue = [&](int kt, auto stage_tag) {
-      constexpr int S = decltype(stage_tag)::value;
-      const int j = (kt * kBN) / kStageRows;
-      if (j >= ready_upto) {
-        // Wait for this tile's flag, then look at all later flags at once (one load per
-        // lane) so the next few tiles need no check.
-        ok &= wave_wait_stamp(a, &flags[j], st, waited);
-        int upto = j + 1;
-        for (int j0 = j + 1; j0 < n_st; j0 += 64) {
-          const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
-          const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
-          if (notready) {
-            upto = j0 + (int)__builtin_ctzll(notready);
-            break;
-          }
-          upto = min(n_st, j0 + 64);
+  // Block vb of the sequence: staged tile known ready, and this wave's slice of it.
+  auto known_ready = [&](int vb) {
+    const bool second = vb >= n0;
+    return vb < nb && ((second ? vb - n0 : vb) * kBN) / kStageRows < (second ? ru1 : ru0);
+  };
+  auto block_w = [&](int vb) {
+    return vb >= n0 ? sblk_w1 + (int64_t)(vb - n0) * Block<D>::kBytes : sblk_w0 + (int64_t)vb * Block<D>::kBytes;
+  };
+  auto issue = [&](int vb, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bool second = vb >= n0;
+    const int j = ((second ? vb - n0 : vb) * kBN) / kStageRows;
+    if (j >= (second ? ru1 : ru0)) {
+      // Wait for this tile's flag, then look at all later flags of its step at once
+      // (one load per lane) so the next few tiles need no check.
+      const int t = t_first + (second ? 1 : 0);
+      const uint64_t* flags = flags_of(t);
+      const uint64_t st = stamp(a.epoch, t);
+      const int n_st = n_tiles_of(t);
+      ok &= wave_wait_stamp(a, &flags[j], st, waited);
+      int upto = j + 1;
+      for (int j0 = j + 1; j0 < n_st; j0 += 64) {
+        const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
+        const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
+        if (notready) {
+          upto = j0 + (int)__builtin_ctzll(notready);
+          break;
         }
-        if (upto > j + 1) fence_acquire();
-        ready_upto = (int)wave_bcast((uint32_t)upto);
+        upto = min(n_st, j0 + 64);
       }
-      dma_block<D, S>(sblk_w + (int64_t)kt * Block<D>::kBytes, cl, m0w_task);
-    };
+      if (upto > j + 1) fence_acquire();
+      upto = (int)wave_bcast((uint32_t)upto);
+      if (second) ru1 = upto;
+      else ru0 = upto;
+    }
+    dma_block<D, S>(block_w(vb), cl, m0w_task);
+  };
 
-    // Online-softmax update for block kt (FlashAttention-2), producing fp16 Pᵀ.
-    auto softmax = [&](int kt) {
-      // Masks: ragged key tail, and keys after the query on the diagonal step.
-      const int k0 = kt * kBN;
-      if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
-        // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
-        // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
-        const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
+  // Online-softmax update for block vb (FlashAttention-2), producing fp16 Pᵀ.
+  auto softmax = [&](int vb) {
+    // Masks: ragged key tail, and keys after the query on the diagonal step.
+    const bool second = vb >= n0;
+    const bool diag = a.causal && t_first == 0 && !second;
+    const int k0 = (second ? vb - n0 : vb) * kBN;
+    if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
+      // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
+      // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
+      const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
-      }
-      // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
-      // fp32 P (four partial sums, short dependency chains) and the PV product takes P
-      // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
-      // the rounded P would not co-issue with the other wave's MFMAs.)
-      float lsum;
-      auto exp_block = [&](float mref) {
-        float ls[4];
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
+    }
+    // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
+    // fp32 P (four partial sums, short dependency chains) and the PV product takes P
+    // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
+    // the rounded P would not co-issue with the other wave's MFMAs.)
+    float lsum;
+    auto exp_block = [&](float mref) {
+      float ls[4];
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-            ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
-            pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
-          }
-        lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      };
-      exp_block(m_run);
-      // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
-      // of its P), or on the first block, is the row max of the block needed: raise
-      // m_run to it, rescale O and l, and redo the block. The max the exponentials use
-      // may therefore lag the true max, by at most log2(kSumMax); every P stays in the
-      // fp16 range and the algebra of the online softmax is unchanged.
-      if (__any(!(lsum <= kSumMax))) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * c2);
-        const float alpha = (m_new == m_run || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
-                                                                   : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-        exp_block(m_run == -INFINITY ? 0.f : m_run);
-      }
-      l_run += lsum;
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
+          ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
+          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
+        }
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
+    exp_block(m_run);
+    // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
+    // of its P), or on the first block, is the row max of the block needed: raise
+    // m_run to it, rescale O and l, and redo the block. The max the exponentials use
+    // may therefore lag the true max, by at most log2(kSumMax); every P stays in the
+    // fp16 range and the algebra of the online softmax is unchanged.
+    if (__any(!(lsum <= kSumMax))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c2);
+      const float alpha = (m_new == m_run || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
+                                                                 : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      exp_block(m_run == -INFINITY ? 0.f : m_run);
+    }
+    l_run += lsum;
+  };
 
-    // Two-phase schedule. Each wave runs M(0) V(0) M(1) V(1) ... M(n_kt), where
-    // M(m) = PV of block m-1 and QKᵀ of block m (matrix cores) and V(m) = the softmax
-    // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
-    // one extra barrier first and group 0 one at the end, so the two waves sharing a
-    // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
-    // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
-    // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
-    // both groups pass only once they are done with it. Before every barrier a wave
-    // waits for its own copies of the next block it or the other group reads; the
-    // barrier then makes every wave's part visible.
-    // Every wave runs every block of the unit: on the diagonal step the blocks past a
-    // wave's last query are fully masked and add exactly zero.
-    //
-    // The compiler may move register-only arithmetic across s_barrier (it orders only
-    // memory), which would pull softmax work into the matrix phase or the reverse and
-    // undo the ping-pong. Empty volatile asm statements, which keep their order with
-    // the barriers, pin each phase's inputs after its barrier and its outputs before
-    // the next one.
-    auto pin_scores = [&]() {
-      if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
-    };
-    auto pin_acc = [&]() {
-      if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
-      else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
-    };
-    auto pin_state = [&]() {
-      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
-      pin_acc();
-    };
-    // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
-    // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
-    // copy is block m+2 when it exists and its staged tile is known to be ready; else it
-    // copies the discard block (one block after the ring slots, always cache-hot, never
-    // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
-    // is seen (same wave, same LDS addresses, completes later). So every wait below has at least one block copy
-    // issued after the one it needs, and waiting until at most NI copy instructions are
-    // outstanding is enough (it may also cover a discarded copy).
-    auto wait_block = [&]() { wait_vm(NI); };
-    // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
-    auto mstep = [&](int m, auto stage_tag, auto mfmas) {
-      constexpr int S = decltype(stage_tag)::value;
-      if (m < n_kt) wait_block();
-      __builtin_amdgcn_s_barrier();
-      const int kn = m + 2;
-      const bool ready = wave_bcast(kn < n_kt && (kn * kBN) / kStageRows < ready_upto) != 0;
-      // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
-      // and instruction offsets here (scalar adds) instead of keeping sixteen of them
-      // in SGPRs across the loop.
-      uint32_t m0w = m0w_task;
-      asm volatile("" : "+s"(m0w));
-      mfmas(ready ? sblk_w + (int64_t)kn * Block<D>::kBytes : discard_w, m0w);
-      pin_scores();
-      pin_acc();
-      if (kn < n_kt && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
-    };
-    auto vstep = [&](int m) {
-      if (m + 1 < n_kt) wait_block();
-      __builtin_amdgcn_s_barrier();
-      pin_scores();
-      softmax(m);
-      pin_state();
-    };
+  // Two-phase schedule. Each wave runs M(0) V(0) M(1) V(1) ... M(nb), where
+  // M(m) = PV of block m-1 and QKᵀ of block m (matrix cores) and V(m) = the softmax
+  // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
+  // one extra barrier first and group 0 one at the end, so the two waves sharing a
+  // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
+  // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
+  // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
+  // both groups pass only once they are done with it. Before every barrier a wave
+  // waits for its own copies of the next block it or the other group reads; the
+  // barrier then makes every wave's part visible.
+  // Every wave runs every block of the unit: on the diagonal step the blocks past a
+  // wave's last query are fully masked and add exactly zero. The sequence runs
+  // straight from the first step's last block into the second step's first.
+  //
+  // The compiler may move register-only arithmetic across s_barrier (it orders only
+  // memory), which would pull softmax work into the matrix phase or the reverse and
+  // undo the ping-pong. Empty volatile asm statements, which keep their order with
+  // the barriers, pin each phase's inputs after its barrier and its outputs before
+  // the next one.
+  auto pin_scores = [&]() {
+    if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+  };
+  auto pin_acc = [&]() {
+    if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+    else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
+  };
+  auto pin_state = [&]() {
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
+    pin_acc();
+  };
+  // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
+  // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
+  // copy is block m+2 when it exists and its staged tile is known to be ready; else it
+  // copies the discard block (one block after the ring slots, always cache-hot, never
+  // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
+  // is seen (same wave, same LDS addresses, completes later). So every wait below has
+  // at least one block copy issued after the one it needs, and waiting until at most
+  // NI copy instructions are outstanding is enough (it may also cover a discarded
+  // copy).
+  auto wait_block = [&]() { wait_vm(NI); };
+  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
+  auto mstep = [&](int m, auto stage_tag, auto mfmas) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (m < nb) wait_block();
+    __builtin_amdgcn_s_barrier();
+    const int kn = m + 2;
+    const bool ready = wave_bcast(known_ready(kn)) != 0;
+    // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
+    // and instruction offsets here (scalar adds) instead of keeping sixteen of them
+    // in SGPRs across the loop.
+    uint32_t m0w = m0w_task;
+    asm volatile("" : "+s"(m0w));
+    mfmas(ready ? block_w(kn) : discard_w, m0w);
+    pin_scores();
+    pin_acc();
+    if (kn < nb && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
+  };
+  auto vstep = [&](int m) {
+    if (m + 1 < nb) wait_block();
+    __builtin_amdgcn_s_barrier();
+    pin_scores();
+    softmax(m);
+    pin_state();
+  };
 #define MKRA_PVQK(S) \
-    [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
+  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
 #define MKRA_PV(S) \
-    [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
-    // n_kt >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
-    // unit's first query).
-    issue(0, std::integral_constant<int, 0>{});
-    if (1 < n_kt) issue(1, std::integral_constant<int, 1>{});
-    else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
-    if (grp) {
-      wait_block();
-      __builtin_amdgcn_s_barrier();
-    }
-    mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
-      MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
-    });
-    vstep(0);
-    int m = 1;
-    for (; m + 3 < n_kt; m += kStages) {
-      mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
+  // nb >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
+  // unit's first query).
+  issue(0, std::integral_constant<int, 0>{});
+  if (1 < nb) issue(1, std::integral_constant<int, 1>{});
+  else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
+  if (grp) {
+    wait_block();
+    __builtin_amdgcn_s_barrier();
+  }
+  mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
+    MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
+  });
+  vstep(0);
+  int m = 1;
+  for (; m + 3 < nb; m += kStages) {
+    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+    vstep(m);
+    mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+    vstep(m + 1);
+    mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
+    vstep(m + 2);
+    mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
+    vstep(m + 3);
+  }
+  if (m < nb) {
+    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
+    vstep(m);
+    if (++m < nb) {
+      mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
       vstep(m);
-      mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
-      vstep(m + 1);
-      mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
-      vstep(m + 2);
-      mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
-      vstep(m + 3);
-    }
-    if (m < n_kt) {
-      mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
-      vstep(m);
-      if (++m < n_kt) {
-        mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
+      if (++m < nb) {
+        mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
         vstep(m);
-        if (++m < n_kt) {
-          mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
-          vstep(m);
-          ++m;
-        }
+        ++m;
       }
     }
-    // M(n_kt): PV of the last block only; no wait follows, so it copies nothing.
-    switch (n_kt & 3) {
-      case 0: mstep(n_kt, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
-      case 1: mstep(n_kt, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
-      case 2: mstep(n_kt, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
-      default: mstep(n_kt, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
-    }
+  }
+  // M(nb): PV of the last block only; no wait follows, so it copies nothing.
+  switch (nb & 3) {
+    case 0: mstep(nb, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
+    case 1: mstep(nb, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
+    case 2: mstep(nb, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
+    default: mstep(nb, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
+  }
 #undef MKRA_PVQK
 #undef MKRA_PV
-    if (!grp) __builtin_amdgcn_s_barrier();
-    // Discarded copies may still be in flight: drain them before this workgroup's next
-    // step, task or staging task writes the same LDS; the barrier keeps the next step's
-    // first copies out of stages that the other group may still be reading.
-    wait_vm(0);
-    if (t + 1 < t_end) __syncthreads();
-  }
+  if (!grp) __builtin_amdgcn_s_barrier();
+  // Discarded copies may still be in flight: drain them before this workgroup's next
+  // task (or staging task) writes the same LDS.
+  wait_vm(0);
+
 
   if (ok && wave_rows) {
     if (t_end == a.n_steps) {
