@@ -33,6 +33,7 @@ namespace mkra {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -766,22 +767,26 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
     }
-    // P = exp2(s c2 - m_run) against the running max as it stands; l sums the exact
-    // fp32 P (four partial sums, short dependency chains) and the PV product takes P
-    // rounded to fp16, which moves O / l by at most 2^-11 max|V|. (A v_dot2c sum of
-    // the rounded P would not co-issue with the other wave's MFMAs.)
+    // P = exp2(s c2 - m_run) against the running max as it stands, rounded to fp16 for
+    // the PV product; l sums the same rounded P, by packed fp16 adds in a tree (15
+    // instructions for 32 values, against 31 fp32 adds; the vector ALU is shared with
+    // the other wave's softmax), the last level in fp32. The tree's rounding moves a
+    // block's sum by about 2^-11 relative per level, independently from block to
+    // block. A sum past the fp16 range becomes inf and takes the rescale path below,
+    // as any sum above kSumMax does. (A v_dot2c sum would not co-issue with the other
+    // wave's MFMAs.)
     float lsum;
     auto exp_block = [&](float mref) {
-      float ls[4];
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-          ls[i & 3] = (kb == 0 && i < 4) ? pv : ls[i & 3] + pv;
-          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)pv;
-        }
-      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        for (int i = 0; i < 16; ++i)
+          pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
+      static_assert(kBN / 16 == 4, "four fp16x8 P vectors");
+      const f16x8 t8 = (pb[0] + pb[1]) + (pb[2] + pb[3]);
+      const f16x4 t4 = __builtin_shufflevector(t8, t8, 0, 1, 2, 3) + __builtin_shufflevector(t8, t8, 4, 5, 6, 7);
+      const f16x2 t2 = __builtin_shufflevector(t4, t4, 0, 1) + __builtin_shufflevector(t4, t4, 2, 3);
+      lsum = (float)t2[0] + (float)t2[1];
     };
     exp_block(m_run);
     // Only when some P of the block exceeds kSumMax (a lane's partial sum bounds each
@@ -856,7 +861,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     if (m < nb) wait_block();
     __builtin_amdgcn_s_barrier();
     const int kn = m + 2;
-    const bool ready = wave_bcast(known_ready(kn)) != 0;
+    const bool ready = known_ready(kn);  // from scalars only: stays in SALU
     // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
     // and instruction offsets here (scalar adds) instead of keeping sixteen of them
     // in SGPRs across the loop.
