@@ -581,6 +581,34 @@ struct MPhase {
     seq(std::make_integer_sequence<int, N>{}, std::make_integer_sequence<int, (LA < N ? LA : N)>{}, la, o, pb, s, qr,
         dma_src, cl, m0w);
   }
+  // The phase's first LA operand reads, issued ahead of it by the same wave at the end
+  // of its softmax phase. They read the Vᵀ of the previous block, which has been
+  // complete and visible since the barrier before the previous matrix phase, so the
+  // MFMAs can start right after this phase's barrier instead of one LDS latency
+  // later.
+  template <int... P>
+  static __device__ __forceinline__ void pre(std::integer_sequence<int, P...>, u32x4 (&buf)[R],
+                                             const LaneAddr<D>& la) {
+    (read<P>(buf, la), ...);
+  }
+  static __device__ __forceinline__ void prefetch(u32x4 (&buf)[R], const LaneAddr<D>& la) {
+    static_assert(PV && LA <= NPV, "the reads issued ahead are PV operands");
+    pre(std::make_integer_sequence<int, LA>{}, buf, la);
+  }
+  template <int... J>
+  static __device__ __forceinline__ void seq_pre(std::integer_sequence<int, J...>, u32x4 (&buf)[R],
+                                                 const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
+                                                 f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+                                                 const CopyLanes<D>& cl, uint32_t m0w) {
+    __builtin_amdgcn_sched_barrier(0);
+    (exec<J>(buf, la, o, pb, s, qr, dma_src, cl, m0w), ...);
+  }
+  // The phase after prefetch(buf) was issued for it.
+  static __device__ __forceinline__ void run_pre(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
+                                                 const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
+                                                 const uint8_t* dma_src, const CopyLanes<D>& cl, uint32_t m0w) {
+    seq_pre(std::make_integer_sequence<int, N>{}, buf, la, o, pb, s, qr, dma_src, cl, m0w);
+  }
 };
 
 template <int D>
@@ -872,17 +900,25 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     pin_acc();
     if (kn < nb && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
   };
-  auto vstep = [&](int m) {
+  // Operand registers of the next matrix phase's first LDS reads, issued at the end of
+  // each softmax phase (MPhase::prefetch).
+  u32x4 pre[MPhase<D, 0, true, true>::R];
+  // V(m), then the first operand reads of M(m+1), whose stage is SN.
+  auto vstep = [&](int m, auto next_stage_tag) {
+    constexpr int SN = decltype(next_stage_tag)::value;
     if (m + 1 < nb) wait_block();
     __builtin_amdgcn_s_barrier();
     pin_scores();
     softmax(m);
     pin_state();
+    MPhase<D, SN, true, true>::prefetch(pre, la);
   };
 #define MKRA_PVQK(S) \
-  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run(la, o, pb, s, qr, src, cl, m0w); }
+  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); }
 #define MKRA_PV(S) \
-  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, false, false>::run(la, o, pb, s, qr, src, cl, m0w); }
+  [&](const uint8_t* src, uint32_t m0w) { \
+    MPhase<D, S, true, false, false>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); \
+  }
   // nb >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
   // unit's first query).
   issue(0, std::integral_constant<int, 0>{});
@@ -895,27 +931,31 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
     MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
   });
-  vstep(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  vstep(0, S1{});
   int m = 1;
   for (; m + 3 < nb; m += kStages) {
-    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
-    vstep(m);
-    mstep(m + 1, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
-    vstep(m + 1);
-    mstep(m + 2, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
-    vstep(m + 2);
-    mstep(m + 3, std::integral_constant<int, 0>{}, MKRA_PVQK(0));
-    vstep(m + 3);
+    mstep(m, S1{}, MKRA_PVQK(1));
+    vstep(m, S2{});
+    mstep(m + 1, S2{}, MKRA_PVQK(2));
+    vstep(m + 1, S3{});
+    mstep(m + 2, S3{}, MKRA_PVQK(3));
+    vstep(m + 2, S0{});
+    mstep(m + 3, S0{}, MKRA_PVQK(0));
+    vstep(m + 3, S1{});
   }
   if (m < nb) {
-    mstep(m, std::integral_constant<int, 1>{}, MKRA_PVQK(1));
-    vstep(m);
+    mstep(m, S1{}, MKRA_PVQK(1));
+    vstep(m, S2{});
     if (++m < nb) {
-      mstep(m, std::integral_constant<int, 2>{}, MKRA_PVQK(2));
-      vstep(m);
+      mstep(m, S2{}, MKRA_PVQK(2));
+      vstep(m, S3{});
       if (++m < nb) {
-        mstep(m, std::integral_constant<int, 3>{}, MKRA_PVQK(3));
-        vstep(m);
+        mstep(m, S3{}, MKRA_PVQK(3));
+        vstep(m, S0{});
         ++m;
       }
     }
