@@ -190,8 +190,12 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
     claimed += steps_claimed(a, units_in_queue(a, x), (int64_t)heads[x]);
   }
   int64_t rp = (int64_t)a.n_units * a.n_steps - claimed;
-  uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
-  uint64_t sd = ld32(&a.ctrl->stage_done.v), stt = ld64(&a.ctrl->stage_ticks.v);
+  // Per-task cost of a role: the time a workgroup spends in it per task, its waits
+  // included (a workgroup waiting for a free slot or a ready tile is held by the role).
+  uint64_t cd = ld32(&a.ctrl->compute_done.v),
+           ct = ld64(&a.ctrl->compute_ticks.v) + ld64(&a.ctrl->compute_wait_ticks.v);
+  uint64_t sd = ld32(&a.ctrl->stage_done.v),
+           stt = ld64(&a.ctrl->stage_ticks.v) + ld64(&a.ctrl->stage_wait_ticks.v);
   int64_t cp = cd ? (int64_t)(ct / cd) : a.cost_compute0;
   int64_t cs = sd ? (int64_t)(stt / sd) : a.cost_stage0;
   if (cp < 1) cp = 1;
