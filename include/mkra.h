@@ -12,9 +12,9 @@
  *
  * Everything runs in ONE persistent kernel per call. Its workgroups (one per compute
  * unit) take one of two roles: compute (the attention steps) or staging (the ring
- * receive: copy each step's KV chunk into a double buffer in HBM, 128-row tile by
- * 128-row tile, in the layout the compute role reads, and publish an epoch-stamped
- * ready flag per tile). An on-GPU controller re-targets the number of staging
+ * receive: copy each step's KV chunk into a ring of four slots in HBM, 128-row tile
+ * by 128-row tile, in the layout the compute role reads, and publish an
+ * epoch-stamped ready flag per tile). An on-GPU controller re-targets the number of staging
  * workgroups with Eq. (2).
  *
  * Conventions for every entry point:
@@ -23,7 +23,7 @@
  *    pointer.
  *  - The caller owns all tensors and must keep them alive until the stream has
  *    passed the call. The library keeps no pointer to them after returning.
- *  - The library owns a workspace per (device, stream): the KV double buffer, ready
+ *  - The library owns a workspace per (device, stream): the KV slot ring, ready
  *    flags, counters, the fp32 accumulator carried between ring steps, and an
  *    optional trace buffer. It grows on demand (synchronising that stream first) and
  *    is freed by mk_release_workspace(). Two calls on one stream run one after the
@@ -131,7 +131,7 @@ typedef struct {
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,
  * v3 wait ticks), 2 staging task (v0 task, v1 step, v2 tile, v3 start tick, v4 1 if
  * done by a stalled compute workgroup, v5 element offset of its destination in the
- * double buffer, -1 if it did not copy), 3 controller update (v0 R_p, v1 R_s, v2 C_p,
+ * slot ring, -1 if it did not copy), 3 controller update (v0 R_p, v1 R_s, v2 C_p,
  * v3 C_s, v4 blocks B, v5 new target), 4 role switch (v0 new role: 0 compute,
  * 1 staging, v1 staging-role count after it). t: tick at which it was written. */
 typedef struct {
@@ -149,7 +149,7 @@ typedef struct {
  *                                   sequence (index 0 = K, 1 = V). kv_chunks[rank] is
  *                                   the local chunk; the others stand for the memory
  *                                   of the other ranks, from which the staging role
- *                                   copies each step's chunk into the double buffer.
+ *                                   copies each step's chunk into the slot ring.
  *  n_chunks   N >= 1 (ring size)
  *  rank       0 <= rank < N
  *  causal     0: every query sees every key. 1: query i sits at global position

@@ -11,7 +11,7 @@ namespace mkra {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-// Keys per KV tile held in LDS (double-buffered).
+// Keys per KV block held in LDS (a ring of kStages blocks).
 constexpr int kBN = 64;
 // Rows of a staged KV tile: the pages' Table 3 moves Ring Attention's KV in tiles of
 // 128 rows; one staging task and one ready flag per (slot, tile).

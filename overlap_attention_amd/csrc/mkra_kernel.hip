@@ -3,10 +3,10 @@
 // One launch runs every ring step of one rank (mKernel paper "mKernel: Fast
 // Multi-GPU, Multi-Node Fused Kernels", §4 / Table 3, Ring Attention row). Its
 // workgroups take roles (§3.2): COMPUTE workgroups run the blockwise
-// FlashAttention forward of a (unit, step) task and carry the online-softmax state
-// (running max m, running sum l, unnormalised O) from step to step; STAGING
-// workgroups play the ring receive on one GPU, copying the chunk of the next step
-// into a double buffer in HBM and publishing an epoch-stamped ready flag per
+// FlashAttention forward of a (unit, step group) task and carry the online-softmax
+// state (running max m, running sum l, unnormalised O) from step to step; STAGING
+// workgroups play the ring receive on one GPU, copying the chunk of a coming step
+// into a ring of four slots in HBM and publishing an epoch-stamped ready flag per
 // 128-row tile (Table 3 granularity; epoch-stamped flags per §4). The target
 // number of staging workgroups follows Eq. (2) of §3.2, recomputed on the GPU from
 // cycle counters; a compute wave stalled on a flag may do a staging task itself.

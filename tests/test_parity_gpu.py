@@ -145,6 +145,29 @@ def test_constant_v_rows_return_v():
     assert err <= 1e-2
 
 
+def test_rising_scores_take_the_rescale_path():
+    """Scores that rise by about 9 nats from each KV block to the next, in ring order:
+    every block after the first drives the lagging running max past its bound, and the
+    packed fp16 row sum of such a block overflows to inf, so the kernel must take the
+    rescale path on every block and still match the oracle."""
+    cfg = shape("rising", 2, 0, 256, 256, 4, 2, 128, False)
+    announce("rising scores: rescale on every block, fp16 row-sum overflow")
+    q, kv = make_inputs(cfg, seed=12)
+    q[:] = 0.5
+    g = torch.Generator().manual_seed(13)
+    order = [0, 1]  # ring order of the chunks for rank 0 of 2: local first, then chunk 1
+    for pos, c in enumerate(order):
+        for j in range(cfg.lk // 64):
+            b = 1.6 * (pos * (cfg.lk // 64) + j)   # 0.5 * 128 * b / sqrt(128) = 5.66 b nats
+            noise = 0.05 * torch.randn((64, cfg.hkv, cfg.d), generator=g)
+            kv[c, 0, 64 * j:64 * (j + 1)] = (b + noise).to(torch.bfloat16)
+    out, lse = run_gpu(q.cuda(), kv.cuda(), cfg)
+    ref_o, ref_l = oracle.ring_attention_reference(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio)
+    rep = compare(to_f64(out), lse.double().cpu().numpy(), ref_o, ref_l)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
+
+
 def test_future_chunks_never_read():
     cfg = shape("poison", 6, 2, 192, 192, 4, 2, 64, True)
     announce("causal poisoning of chunks after the rank")
