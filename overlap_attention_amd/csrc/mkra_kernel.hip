@@ -615,8 +615,11 @@ struct MPhase {
   }
 };
 
-template <int D>
-__device__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited) {
+// claim_next() picks the workgroup's next task (wave 0); it runs while this task's
+// state stores drain, before the publish.
+template <int D, class ClaimNext>
+__device__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
+                             ClaimNext&& claim_next) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int NI = Block<D>::kChunksPerThread;  // block-copy instructions per wave per tile
@@ -1010,6 +1013,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
       reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, 0.f, 0.f};
     }
   }
+  // The next claim (a few dependent memory round trips for wave 0) overlaps the drain
+  // of the stores above; the publish below still precedes the next task.
+  claim_next();
   // Publish: unit steps done (orders the state for the next group) and slot release for
   // each step of the task. Every wave's stores precede the barrier; one agent-scope
   // release fence by thread 0 covers them and every signal after it. (A wave whose
@@ -1230,16 +1236,21 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
     sched.pending = 0;
   }
 
+  bool claimed = false;  // the compute task that just ended already claimed the next one
   while (true) {
     __syncthreads();
-    if (tid < 64) schedule(kernel_args(), &sched, g_cmd);
+    if (!claimed && tid < 64) schedule(kernel_args(), &sched, g_cmd);
+    claimed = false;
     __syncthreads();
     const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
     if (op == kOpExit) break;
     if (op == kOpCompute) {
       const uint64_t t0 = ticks();
       uint64_t w0 = 0;
-      compute_task<D>(a, x, y, grp, w0);
+      compute_task<D>(a, x, y, grp, w0, [&]() {
+        if (tid < 64) schedule(kernel_args(), &sched, g_cmd);
+      });
+      claimed = true;
       if (tid == 0) {
         const uint64_t busy = ticks() - t0 - w0;
         const int t_first = y * kGroup, t_end = min(a.n_steps, t_first + kGroup);
