@@ -260,6 +260,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kLdsBytes = kStages * Block<128>::kBytes;
 __shared__ __attribute__((aligned(16))) uint8_t g_lds[kLdsBytes];
 __shared__ int32_t g_cmd[4];
+// Waves of the workgroup whose stores of the finished compute task are complete (the
+// publish handshake at the end of a compute task).
+__shared__ uint32_t g_pub_count;
 
 template <int D, int S>
 constexpr int stage_k() { return S * Block<D>::kKBytes; }
@@ -615,8 +618,7 @@ struct MPhase {
   }
 };
 
-// claim_next() picks the workgroup's next task (wave 0); it runs while this task's
-// state stores drain, before the publish.
+// claim_next() picks the workgroup's next task (wave 1); it runs alongside the publish.
 template <int D, class ClaimNext>
 __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
                              ClaimNext&& claim_next) {
@@ -1013,16 +1015,25 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
       reinterpret_cast<f32x4*>(accw + 32 * D)[lane] = f32x4{m_run, l_run, 0.f, 0.f};
     }
   }
-  // The next claim (a few dependent memory round trips for wave 0) overlaps the drain
-  // of the stores above; the publish below still precedes the next task.
-  claim_next();
   // Publish: unit steps done (orders the state for the next group) and slot release for
-  // each step of the task. Every wave's stores precede the barrier; one agent-scope
-  // release fence by thread 0 covers them and every signal after it. (A wave whose
-  // wait failed has raised the launch's error; publishing after another workgroup's
-  // error is harmless, since every wait ends on it.)
+  // each step of the task. Each wave waits for its own stores and counts itself in
+  // (workgroup-scope release); thread 0 waits for all eight, then one agent-scope
+  // release fence covers every wave's stores and the signals after it. Meanwhile
+  // wave 1 claims the next task: its few dependent memory round trips overlap the
+  // publish instead of delaying it, which matters when a unit's chain of steps is the
+  // critical path. (A wave whose wait failed has raised the launch's error; publishing
+  // after another workgroup's error is harmless, since every wait ends on it.)
+  wait_vm(0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
+  if (lane == 0) __hip_atomic_fetch_add(&g_pub_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  claim_next();
+  if (tid == 0) {
+    // Bounded: every wave counts itself in once its own stores are done.
+    while (__hip_atomic_load(&g_pub_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)kWaves)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __hip_atomic_store(&g_pub_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   if (tid == 0 && ok) {
     fence_release();
     __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t_end - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1234,6 +1245,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   if (tid == 0) {
     sched.role = (int32_t)role;
     sched.pending = 0;
+    g_pub_count = 0;
   }
 
   bool claimed = false;  // the compute task that just ended already claimed the next one
@@ -1248,7 +1260,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       const uint64_t t0 = ticks();
       uint64_t w0 = 0;
       compute_task<D>(a, x, y, grp, w0, [&]() {
-        if (tid < 64) schedule(kernel_args(), &sched, g_cmd);
+        if (tid >= 64 && tid < 128) schedule(kernel_args(), &sched, g_cmd);
       });
       claimed = true;
       if (tid == 0) {
