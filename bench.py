@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--workload NAME]
                     [--no-cpu-baseline] [--sweep] [--size-sweep] [--verify] [--copy-calibration-mib M]
     python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
+    python bench.py --probes    (MFMA-stream and vector-ALU probes; prints a table)
 
 A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
 rank, staging included) over one batch of synthetic input already resident in HBM.
@@ -198,6 +199,51 @@ def run_size_sweep(torch, mk, make_inputs, stream):
     return out
 
 
+PROBE_MODES = (
+    (2, "MFMA + ds_read_b128, random bf16"),
+    (0, "MFMA, random bf16 from registers"),
+    (1, "MFMA + ds_read_b128, constant data"),
+    (3, "MFMA + ds_read_b128, random bf16, + exp2 and FMA per MFMA"),
+)
+
+
+def run_probes(rounds=3):
+    """Runs libmkra_probes.so: MFMA streams (8 waves per CU, about 0.2 s per launch, the
+    modes in turn, `rounds` times; median per mode) and the v_exp_f32 / v_fma_f32 issue
+    rates. Returns markdown."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "overlap_attention_amd", "libmkra_probes.so"))
+    for fn in (lib.mkp_mfma_stream, lib.mkp_valu_rate):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+        fn.restype = ctypes.c_int
+
+    def call(fn, mode, iters):
+        res = (ctypes.c_double * 4)()
+        if fn(mode, iters, res) != 0:
+            raise RuntimeError("probe failed (mode %d)" % mode)
+        return list(res)
+
+    rows = {m: [] for m, _ in PROBE_MODES}
+    for r in range(rounds):
+        for m, name in PROBE_MODES:
+            rows[m].append(call(lib.mkp_mfma_stream, m, 150000))
+            log(f"[probes] round {r} mode {m}: {rows[m][-1][2]:.0f} TFLOP/s at {rows[m][-1][1]:.3f} GHz")
+    out = ["| MFMA stream (v_mfma_f32_32x32x16_bf16, 8 waves per CU) | ms | shader clock GHz | TFLOP/s | "
+           "% of 2.4 GHz peak | % of peak at its clock |", "|---|---:|---:|---:|---:|---:|"]
+    for m, name in PROBE_MODES:
+        ms, ghz, tf, _ = sorted(rows[m], key=lambda x: x[2])[len(rows[m]) // 2]
+        out.append(f"| {name} | {ms:.1f} | {ghz:.3f} | {tf:.0f} | {100 * tf / PEAK_BF16_TFLOPS:.1f} | "
+                   f"{100 * tf / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ):.1f} |")
+    out += ["", "| vector op (8 independent chains per lane, 8 waves per CU) | ms | shader clock GHz | "
+            "lane-ops per clock per CU |", "|---|---:|---:|---:|"]
+    for m, name in ((0, "v_exp_f32"), (1, "v_fma_f32")):
+        ms, ghz, rate, _ = call(lib.mkp_valu_rate, m, 200000)
+        log(f"[probes] {name}: {rate:.1f} lane-ops/clk/CU")
+        out.append(f"| {name} | {ms:.1f} | {ghz:.3f} | {rate:.1f} |")
+    return "\n".join(out)
+
+
 def cpu_baseline(cfg, q, kv, budget_rows):
     """The fp64 oracle on the host cores, on a bounded sample of the same workload:
     `budget_rows` query rows spread over the chunk, all heads, all keys."""
@@ -261,7 +307,12 @@ def main():
     ap.add_argument("--traffic-from", default=None,
                     help="no GPU: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs (DIR/fetch, DIR/write) into "
                          "profiles/traffic_<workload>.json")
+    ap.add_argument("--probes", action="store_true",
+                    help="run the MFMA-stream and vector-ALU probes instead of the benchmark; prints markdown")
     args = ap.parse_args()
+    if args.probes:
+        print(run_probes(), flush=True)
+        return
     if args.traffic_from:
         from ring_inputs import CONFIGS, CONFIG_BY_NAME
 

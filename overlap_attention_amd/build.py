@@ -1,4 +1,5 @@
-"""Builds the in-tree HIP library overlap_attention_amd/libmkra.so for gfx950.
+"""Builds the in-tree HIP libraries for gfx950: overlap_attention_amd/libmkra.so (the
+ring-attention path) and libmkra_probes.so (measurement probes that bench.py runs).
 
 Usage: python -m overlap_attention_amd.build   (or overlap_attention_amd.build.build())
 """
@@ -11,6 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmkra.so")
 SOURCES = [os.path.join(HERE, "csrc", "mkra_kernel.hip"), os.path.join(HERE, "csrc", "mkra_api.cpp")]
+PROBES_LIB = os.path.join(HERE, "libmkra_probes.so")
+PROBES_SOURCES = [os.path.join(HERE, "csrc", "mkra_probes.hip")]
 
 # All HIP code is built without packed-FP32 instructions.
 FLAGS = [
@@ -27,16 +30,21 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + SOURCES + ["-o", tmp]
+def _build_one(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [hipcc()] + FLAGS + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("building libmkra.so failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError("building %s failed" % os.path.basename(lib))
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    _build_one(SOURCES, LIB, verbose)
+    _build_one(PROBES_SOURCES, PROBES_LIB, verbose)
     return LIB
 
 
