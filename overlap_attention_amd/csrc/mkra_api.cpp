@@ -261,7 +261,10 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   if (n_units > (1 << 26)) return fail(MK_E_INVAL, "too many compute units");
   a.n_units = (int)n_units;
   a.n_tiles = (int)((lk + mkra::kStageRows - 1) / mkra::kStageRows);
-  a.n_blocks = (int)((lk + mkra::kBN - 1) / mkra::kBN);
+  // Blocks per KV head, padded to whole tiles: a tile always stages kStageRows / kBN
+  // blocks (keys past Lk as zeros), so a compute phase of two blocks (D = 64) never
+  // reaches past its head's blocks.
+  a.n_blocks = a.n_tiles * (mkra::kStageRows / mkra::kBN);
   // Every step's chunk, the local one included, is staged once into the layout the
   // compute role reads.
   const int64_t n_stage_tasks = (int64_t)n_steps * a.n_tiles;

@@ -143,7 +143,7 @@ struct KernelArgs {
   // Staging work: tasks = (step 0..S-1) x (128-row tile); each step's chunk is staged
   // into slot step % 2 as blocks of 64 keys per KV head.
   int n_tiles;            // ceil(Lk / 128)
-  int n_blocks;           // ceil(Lk / 64): blocks per KV head
+  int n_blocks;           // 2 * n_tiles: blocks per KV head (keys past Lk staged as zeros)
   int n_stage_tasks;
   int64_t chunk_elems;    // 2 * Lk * Hkv * D: one chunk in kv_chunks
   int64_t slot_bytes;     // Hkv * n_blocks * block bytes

@@ -250,6 +250,25 @@ __device__ bool wave_wait_stamp(const KernelArgs& a, const uint64_t* p, uint64_t
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// A phase of the compute role covers Phase<D>::kBlocks consecutive staged blocks of
+// one KV head (1 or 2; the blocks of a 128-row staged tile are adjacent in the slot,
+// so a phase is one contiguous copy whose blocks' K parts land side by side in the
+// stage's K region, one K matrix of kKeys rows, and their Vᵀ parts side by side in
+// its Vᵀ region). Two blocks per phase at D = 64 (32 products per phase, as at
+// D = 128) passed the parity tests but ran 8% slower on the 32K-token MHA workload
+// than one, so every head size runs one block per phase.
+template <int D>
+struct Phase {
+  static constexpr int kBlocks = 1;
+  static constexpr int kKeys = kBlocks * kBN;
+  static constexpr int kBytes = kBlocks * Block<D>::kBytes;
+  static constexpr int kKBytes = kBlocks * Block<D>::kKBytes;  // K (or Vᵀ) region of a stage
+  static constexpr int kChunksPerThread = kBytes / 16 / kThreads;
+};
+static_assert(Phase<64>::kBytes <= Phase<128>::kBytes, "the LDS ring is sized for D = 128");
+static_assert(Phase<64>::kKeys <= kStageRows && kStageRows % Phase<64>::kKeys == 0, "a phase lies in one staged tile");
+
+
 // The compute role's LDS ring of kStages staged KV blocks: the K parts of stages 0..3
 // first, then their Vᵀ parts (stage_k / stage_v byte offsets), so every operand read
 // reaches its stage with one per-lane address register and the 16-bit offset field.
@@ -257,7 +276,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (lds_read16) with explicit waits: the compiler cannot tell which stage a block copy
 // in flight writes and would otherwise wait for every copy before any LDS read. A
 // staging task borrows the same memory as scratch for its transposes (scratch_buf).
-constexpr int kLdsBytes = kStages * Block<128>::kBytes;
+constexpr int kLdsBytes = kStages * Phase<128>::kBytes;
 __shared__ __attribute__((aligned(16))) uint8_t g_lds[kLdsBytes];
 __shared__ int32_t g_cmd[4];
 // Waves of the workgroup whose stores of the finished compute task are complete (the
@@ -265,9 +284,9 @@ __shared__ int32_t g_cmd[4];
 __shared__ uint32_t g_pub_count;
 
 template <int D, int S>
-constexpr int stage_k() { return S * Block<D>::kKBytes; }
+constexpr int stage_k() { return S * Phase<D>::kKBytes; }
 template <int D, int S>
-constexpr int stage_v() { return (kStages + S) * Block<D>::kKBytes; }
+constexpr int stage_v() { return (kStages + S) * Phase<D>::kKBytes; }
 
 template <int B>
 __device__ __forceinline__ uint8_t* scratch_buf() {
@@ -474,7 +493,7 @@ __device__ __forceinline__ const uint8_t* wave_bcast_ptr(const uint8_t* p) {
 // 16 bytes at I * kThreads * 16 + 16 * lane of the wave's slice.
 template <int D>
 struct CopyLanes {
-  uint32_t off[Block<D>::kChunksPerThread];
+  uint32_t off[Phase<D>::kChunksPerThread];
 };
 
 // Copy instruction I of a staged block into LDS stage S: each wave moves 1 KB per
@@ -488,10 +507,13 @@ struct CopyLanes {
 // other wave's softmax).
 template <int D, int S, int I>
 __device__ __forceinline__ void dma_one(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w) {
-  constexpr int kHalf = Block<D>::kChunks / 2;  // chunks of the K part
-  static_assert(kHalf % kThreads == 0, "one instruction copies K or V, not both");
-  constexpr int kDst = I * kThreads < kHalf ? stage_k<D, S>() + I * kThreads * 16
-                                            : stage_v<D, S>() + (I * kThreads - kHalf) * 16;
+  // Instruction I moves bytes [I, I+1) * kThreads * 16 of the phase: part x of its
+  // block b, a K part or a Vᵀ part (never both).
+  constexpr int kSrc = I * kThreads * 16;
+  constexpr int b = kSrc / Block<D>::kBytes, x = kSrc % Block<D>::kBytes;
+  static_assert(Block<D>::kKBytes % (kThreads * 16) == 0, "one instruction copies K or V, not both");
+  constexpr int kDst = x < Block<D>::kKBytes ? stage_k<D, S>() + b * Block<D>::kKBytes + x
+                                             : stage_v<D, S>() + b * Block<D>::kKBytes + (x - Block<D>::kKBytes);
   const uint32_t m0 = m0w + (uint32_t)kDst;
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(cl.off[I]), "s"(src_w), "{m0}"(m0) : "memory");
 }
@@ -502,10 +524,10 @@ __device__ __forceinline__ void dma_seq(const uint8_t* src_w, const CopyLanes<D>
   (dma_one<D, S, I>(src_w, cl, m0w), ...);
 }
 
-// The whole block: Block<D>::kChunksPerThread instructions per wave.
+// The whole phase: Phase<D>::kChunksPerThread instructions per wave.
 template <int D, int S>
 __device__ __forceinline__ void dma_block(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w) {
-  dma_seq<D, S>(src_w, cl, m0w, std::make_integer_sequence<int, Block<D>::kChunksPerThread>{});
+  dma_seq<D, S>(src_w, cl, m0w, std::make_integer_sequence<int, Phase<D>::kChunksPerThread>{});
 }
 
 // Per-lane LDS addresses of the compute role's operand reads (stage 0, block row 0):
@@ -524,22 +546,28 @@ struct LaneAddr {
 template <int D, int S, bool PV, bool QK, bool COPY = true>
 struct MPhase {
   static constexpr int KK = D / 16, DB = D / 32;
-  static constexpr int NPV = PV ? DB * 4 : 0;
-  static constexpr int NQK = QK ? 2 * KK : 0;
+  static constexpr int NP = Phase<D>::kKeys / 16;  // Pᵀ slices (16 keys) of a phase
+  static constexpr int NS = Phase<D>::kKeys / 32;  // Sᵀ tiles (32 keys) of a phase
+  static constexpr int NPV = PV ? DB * NP : 0;
+  static constexpr int NQK = QK ? NS * KK : 0;
   static constexpr int N = NPV + NQK;
   static constexpr int LA = MKRA_LDS_AHEAD;  // LDS reads in flight ahead of the MFMA using the oldest
   static constexpr int R = LA + 2;  // operand registers: a read refills the one used two MFMAs ago
   static constexpr int SPV = (S + kStages - 1) % kStages;
 
+  // PV product J: rows 32 (J / NP) .. of Oᵀ against Pᵀ slice J % NP, which is slice
+  // (J % NP) % 4 of the phase's block (J % NP) / 4. QK product J: Sᵀ tile (J-NPV) / KK
+  // (32 rows of the stage's K matrix) against k-slice (J-NPV) % KK.
   template <int J>
   static constexpr int offset() {
-    if constexpr (J < NPV) return stage_v<D, SPV>() - stage_v<D, 0>() + (J / 4) * 32 * 128;
+    if constexpr (J < NPV)
+      return stage_v<D, SPV>() - stage_v<D, 0>() + ((J % NP) / 4) * Block<D>::kKBytes + (J / NP) * 32 * 128;
     else return stage_k<D, S>() + ((J - NPV) / KK) * 32 * (D * 2);
   }
   template <int J>
   static __device__ __forceinline__ void read(u32x4 (&buf)[R], const LaneAddr<D>& la) {
     if constexpr (J < N) {
-      if constexpr (J < NPV) buf[J % R] = lds_read16<offset<J>()>(la.v[J % 4]);
+      if constexpr (J < NPV) buf[J % R] = lds_read16<offset<J>()>(la.v[(J % NP) % 4]);
       else buf[J % R] = lds_read16<offset<J>()>(la.k[(J - NPV) % KK]);
     }
   }
@@ -547,7 +575,7 @@ struct MPhase {
   // (2I+1) N / (2 NI), so no wave issues several copies at once and waits for the
   // memory pipeline to take them. It is unconditional (a branch here would put vector
   // ALU work for its condition into the stream).
-  static constexpr int NI = Block<D>::kChunksPerThread;
+  static constexpr int NI = Phase<D>::kChunksPerThread;
   template <int J>
   static constexpr int dma_at() {
     for (int i = 0; i < NI; ++i)
@@ -556,12 +584,12 @@ struct MPhase {
   }
   template <int J>
   static __device__ __forceinline__ void exec(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
-                                              const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
+                                              const f16x8 (&pb)[NP], f32x16 (&s)[NS], const bf16x8 (&qr)[KK],
                                               const uint8_t* dma_src, const CopyLanes<D>& cl, uint32_t m0w) {
     constexpr int newer = (N - 1 - J) < (LA - 1) ? (N - 1 - J) : (LA - 1);
     lgkm_wait<newer>(buf[J % R]);
     if constexpr (J < NPV) {
-      constexpr int db = J / 4, pp = J % 4;
+      constexpr int db = J / NP, pp = J % NP;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, buf[J % R]), pb[pp], o[db], 0, 0, 0);
     } else {
       constexpr int kb = (J - NPV) / KK, kk = (J - NPV) % KK;
@@ -574,16 +602,16 @@ struct MPhase {
   }
   template <int... J, int... P>
   static __device__ __forceinline__ void seq(std::integer_sequence<int, J...>, std::integer_sequence<int, P...>,
-                                             const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
-                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+                                             const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[NP],
+                                             f32x16 (&s)[NS], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
                                              const CopyLanes<D>& cl, uint32_t m0w) {
     u32x4 buf[R];
     __builtin_amdgcn_sched_barrier(0);
     (read<P>(buf, la), ...);
     (exec<J>(buf, la, o, pb, s, qr, dma_src, cl, m0w), ...);
   }
-  static __device__ __forceinline__ void run(const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
-                                             f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+  static __device__ __forceinline__ void run(const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[NP],
+                                             f32x16 (&s)[NS], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
                                              const CopyLanes<D>& cl, uint32_t m0w) {
     seq(std::make_integer_sequence<int, N>{}, std::make_integer_sequence<int, (LA < N ? LA : N)>{}, la, o, pb, s, qr,
         dma_src, cl, m0w);
@@ -604,15 +632,15 @@ struct MPhase {
   }
   template <int... J>
   static __device__ __forceinline__ void seq_pre(std::integer_sequence<int, J...>, u32x4 (&buf)[R],
-                                                 const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[4],
-                                                 f32x16 (&s)[2], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
+                                                 const LaneAddr<D>& la, f32x16 (&o)[DB], const f16x8 (&pb)[NP],
+                                                 f32x16 (&s)[NS], const bf16x8 (&qr)[KK], const uint8_t* dma_src,
                                                  const CopyLanes<D>& cl, uint32_t m0w) {
     __builtin_amdgcn_sched_barrier(0);
     (exec<J>(buf, la, o, pb, s, qr, dma_src, cl, m0w), ...);
   }
   // The phase after prefetch(buf) was issued for it.
   static __device__ __forceinline__ void run_pre(u32x4 (&buf)[R], const LaneAddr<D>& la, f32x16 (&o)[DB],
-                                                 const f16x8 (&pb)[4], f32x16 (&s)[2], const bf16x8 (&qr)[KK],
+                                                 const f16x8 (&pb)[NP], f32x16 (&s)[NS], const bf16x8 (&qr)[KK],
                                                  const uint8_t* dma_src, const CopyLanes<D>& cl, uint32_t m0w) {
     seq_pre(std::make_integer_sequence<int, N>{}, buf, la, o, pb, s, qr, dma_src, cl, m0w);
   }
@@ -624,7 +652,9 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
                              ClaimNext&& claim_next) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
-  constexpr int NI = Block<D>::kChunksPerThread;  // block-copy instructions per wave per tile
+  constexpr int NI = Phase<D>::kChunksPerThread;  // copy instructions per wave per phase
+  constexpr int PK = Phase<D>::kKeys;             // keys per phase
+  constexpr int NS = PK / 32, NP = PK / 16;       // Sᵀ tiles and Pᵀ slices per phase
 
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, col = lane & 31;
   const int w = (int)wave_bcast((uint32_t)(tid >> 6));  // wave-uniform, kept in SGPRs
@@ -679,7 +709,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   // per-lane offsets in VGPRs that the compiler may not recompute inside the matrix
   // phase). The discard block follows the ring slots.
   const uint8_t* const discard_w = wave_bcast_ptr(a.slots + kSlots * a.slot_bytes + w * 64 * 16);
-  static_assert(Block<D>::kBytes <= kDiscardBytes, "discard block");
+  static_assert(Phase<D>::kBytes <= kDiscardBytes, "discard block");
   CopyLanes<D> cl;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -687,19 +717,19 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     asm volatile("" : "+v"(cl.off[i]));
   }
   const uint32_t m0w_task = lds_base() + (uint32_t)w * 64u * 16u;
-  // Sᵀ of the current block (registers) and Pᵀ of the block before it (fp16).
-  f32x16 s[kBN / 32];
-  f16x8 pb[kBN / 16];
+  // Sᵀ of the current phase (registers) and Pᵀ of the phase before it (fp16).
+  f32x16 s[NS];
+  f16x8 pb[NP];
 
-  // The task's KV blocks form one sequence: the n0 blocks of step t_first, then those
-  // of step t_first + 1 (kGroup = 2). The online softmax does not depend on where one
+  // The task's KV phases (PK keys each) form one sequence: the n0 phases of step
+  // t_first, then those of step t_first + 1 (kGroup = 2). The online softmax does not depend on where one
   // step ends, so one pipeline runs through both steps without draining in between.
   static_assert(kGroup == 2, "the block sequence covers two steps");
   auto kend_of = [&](int t) { return (a.causal && t == 0) ? min(a.lk, q_end) : a.lk; };
   auto n_tiles_of = [&](int t) { return (kend_of(t) + kStageRows - 1) / kStageRows; };
   const bool two = t_end - t_first > 1;
-  const int n0 = (kend_of(t_first) + kBN - 1) / kBN;
-  const int nb = n0 + (two ? (kend_of(t_first + 1) + kBN - 1) / kBN : 0);
+  const int n0 = (kend_of(t_first) + PK - 1) / PK;
+  const int nb = n0 + (two ? (kend_of(t_first + 1) + PK - 1) / PK : 0);
   const int64_t head_off = (int64_t)kvh * a.n_blocks * Block<D>::kBytes + w * 64 * 16;
   const uint8_t* const sblk_w0 = wave_bcast_ptr(a.slots + (int64_t)(t_first % kSlots) * a.slot_bytes + head_off);
   const uint8_t* const sblk_w1 =
@@ -753,15 +783,15 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   // Block vb of the sequence: staged tile known ready, and this wave's slice of it.
   auto known_ready = [&](int vb) {
     const bool second = vb >= n0;
-    return vb < nb && ((second ? vb - n0 : vb) * kBN) / kStageRows < (second ? ru1 : ru0);
+    return vb < nb && ((second ? vb - n0 : vb) * PK) / kStageRows < (second ? ru1 : ru0);
   };
   auto block_w = [&](int vb) {
-    return vb >= n0 ? sblk_w1 + (int64_t)(vb - n0) * Block<D>::kBytes : sblk_w0 + (int64_t)vb * Block<D>::kBytes;
+    return vb >= n0 ? sblk_w1 + (int64_t)(vb - n0) * Phase<D>::kBytes : sblk_w0 + (int64_t)vb * Phase<D>::kBytes;
   };
   auto issue = [&](int vb, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const bool second = vb >= n0;
-    const int j = ((second ? vb - n0 : vb) * kBN) / kStageRows;
+    const int j = ((second ? vb - n0 : vb) * PK) / kStageRows;
     if (j >= (second ? ru1 : ru0)) {
       // Wait for this tile's flag, then look at all later flags of its step at once
       // (one load per lane) so the next few tiles need no check.
@@ -793,16 +823,24 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     // Masks: ragged key tail, and keys after the query on the diagonal step.
     const bool second = vb >= n0;
     const bool diag = a.causal && t_first == 0 && !second;
-    const int k0 = (second ? vb - n0 : vb) * kBN;
-    if (k0 + kBN > a.lk || (diag && k0 + kBN - 1 > q0w)) {
+    const int k0 = (second ? vb - n0 : vb) * PK;
+    if (k0 + PK > a.lk || (diag && k0 + PK - 1 > q0w)) {
       // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
       // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
       const int lim = (diag ? min(a.lk, qrow + 1) : a.lk) - k0 - hi * 4;
+      // s = min(s, bias) with bias = +inf for a visible key and -inf otherwise, the
+      // sign of (offset - lim) picking the sign of the infinity: a compare per element
+      // would write a scalar register pair, and with 64 of them in flight the scalar
+      // registers of the whole loop spill.
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + (i >> 2) * 8 + (i & 3) >= lim) s[kb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t neg = (uint32_t)(kb * 32 + (i >> 2) * 8 + (i & 3) - lim) & 0x80000000u;  // set iff visible
+          float bias = __builtin_bit_cast(float, 0xff800000u ^ neg);
+          asm volatile("" : "+v"(bias));
+          s[kb][i] = fminf(s[kb][i], bias);
+        }
     }
     // P = exp2(s c2 - m_run) against the running max as it stands, rounded to fp16 for
     // the PV product; l sums the same rounded P, by packed fp16 adds in a tree (15
@@ -815,12 +853,13 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     float lsum;
     auto exp_block = [&](float mref) {
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           pb[kb * 2 + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -mref));
-      static_assert(kBN / 16 == 4, "four fp16x8 P vectors");
-      const f16x8 t8 = (pb[0] + pb[1]) + (pb[2] + pb[3]);
+      static_assert(NP == 4 || NP == 8, "four or eight fp16x8 P vectors");
+      f16x8 t8 = (pb[0] + pb[1]) + (pb[2] + pb[3]);
+      if constexpr (NP == 8) t8 += (pb[4] + pb[5]) + (pb[6] + pb[7]);
       const f16x4 t4 = __builtin_shufflevector(t8, t8, 0, 1, 2, 3) + __builtin_shufflevector(t8, t8, 4, 5, 6, 7);
       const f16x2 t2 = __builtin_shufflevector(t4, t4, 0, 1) + __builtin_shufflevector(t4, t4, 2, 3);
       lsum = (float)t2[0] + (float)t2[1];
@@ -834,7 +873,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     if (__any(!(lsum <= kSumMax))) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = max3(mx, s[kb][i], s[kb][i + 1]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -872,7 +911,8 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   // the barriers, pin each phase's inputs after its barrier and its outputs before
   // the next one.
   auto pin_scores = [&]() {
-    if constexpr (kBN / 32 == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    if constexpr (NS == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    else asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
   };
   auto pin_acc = [&]() {
     if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
@@ -880,6 +920,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   };
   auto pin_state = [&]() {
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
+    if constexpr (NP == 8) asm volatile("" : "+v"(pb[4]), "+v"(pb[5]), "+v"(pb[6]), "+v"(pb[7]));
     pin_acc();
   };
   // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
