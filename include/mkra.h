@@ -12,7 +12,7 @@
  *
  * Everything runs in ONE persistent kernel per call. Its workgroups (one per compute
  * unit) take one of two roles: compute (the attention steps) or staging (the ring
- * receive: copy each step's KV chunk into a ring of four slots in HBM, 128-row tile
+ * receive: copy each step's KV chunk into a ring of eight slots in HBM, 128-row tile
  * by 128-row tile, in the layout the compute role reads, and publish an
  * epoch-stamped ready flag per tile). An on-GPU controller re-targets the number of staging
  * workgroups with Eq. (2).

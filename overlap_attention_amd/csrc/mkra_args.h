@@ -19,13 +19,16 @@ constexpr int kStageRows = 128;
 // LDS pipeline depth of the compute role: KV blocks in flight per workgroup.
 constexpr int kStages = 4;
 // Ring slots in HBM: step t is staged into slot t % kSlots, which is free once every
-// unit has finished step t - kSlots.
-constexpr int kSlots = 4;
+// unit has finished step t - kSlots. Eight slots (C3: 8 x 16.8 MB of the 288 GB) let
+// the staging role run up to three step groups ahead of the slowest unit, so a group's
+// tiles need not all be staged within one group's compute time.
+constexpr int kSlots = 8;
 // Ring steps per compute task: a task runs kGroup consecutive steps of one unit with
 // the running state in registers, so the state is stored and reloaded, and a task
 // claimed, once per kGroup steps. A task of group g needs steps kGroup*g .. staged,
-// which needs every unit past step kGroup*g + kGroup - 1 - kSlots, i.e. group g-2
-// complete when kSlots = 2*kGroup: one group of claim look-ahead stays deadlock-free.
+// which needs every unit past step kGroup*g + kGroup - 1 - kSlots, i.e. group
+// g - kSlots/kGroup complete (g-2 or earlier): one group of claim look-ahead stays
+// deadlock-free.
 constexpr int kGroup = 2;
 static_assert(kSlots >= 2 * kGroup, "a group task may depend only on groups <= g-2");
 // Bytes after the ring slots that the compute role's discarded block copies read

@@ -6,7 +6,7 @@
 // FlashAttention forward of a (unit, step group) task and carry the online-softmax
 // state (running max m, running sum l, unnormalised O) from step to step; STAGING
 // workgroups play the ring receive on one GPU, copying the chunk of a coming step
-// into a ring of four slots in HBM and publishing an epoch-stamped ready flag per
+// into a ring of eight slots in HBM and publishing an epoch-stamped ready flag per
 // 128-row tile (Table 3 granularity; epoch-stamped flags per §4). The target
 // number of staging workgroups follows Eq. (2) of §3.2, recomputed on the GPU from
 // cycle counters; a compute wave stalled on a flag may do a staging task itself.
@@ -190,10 +190,12 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
     claimed += steps_claimed(a, units_in_queue(a, x), (int64_t)heads[x]);
   }
   int64_t rp = (int64_t)a.n_units * a.n_steps - claimed;
-  // Per-task cost of a role: the time a workgroup spends in it per task, its waits
-  // included (a workgroup waiting for a free slot or a ready tile is held by the role).
-  uint64_t cd = ld32(&a.ctrl->compute_done.v),
-           ct = ld64(&a.ctrl->compute_ticks.v) + ld64(&a.ctrl->compute_wait_ticks.v);
+  // Per-task cost of a role. Staging: its busy time plus its waits for a free slot
+  // (slots free at the pace of the compute role, so that wait is part of what a
+  // staging task costs). Compute: its busy time only. A compute task waits for tiles
+  // the staging role has not delivered yet; counted as compute cost, that wait would
+  // shift workgroups away from staging exactly when staging lags.
+  uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
   uint64_t sd = ld32(&a.ctrl->stage_done.v),
            stt = ld64(&a.ctrl->stage_ticks.v) + ld64(&a.ctrl->stage_wait_ticks.v);
   int64_t cp = cd ? (int64_t)(ct / cd) : a.cost_compute0;
@@ -1111,8 +1113,9 @@ struct Sched {
 // read the same KV head share an L2. A workgroup takes from its own queue only while
 // that queue is at most one group ahead of the slowest queue, else from the slowest
 // queue. A task of group g needs its unit's group g-1 (claimed earlier, same queue
-// order) and staging of its steps, whose slots are released once group g-2 is complete
-// (kSlots = 2 kGroup); every task of group g-2 is claimed when the rule admits group
+// order) and staging of its steps, whose slots are released once group g - kSlots/kGroup
+// is complete (at most g-2, as kSlots >= 2 kGroup); every task of group g-2 is claimed
+// when the rule admits group
 // g, so the schedule cannot deadlock whatever subset of workgroups is resident. Within
 // a group a queue runs its units from the last, so on the causal diagonal step the
 // longest query blocks start first.
