@@ -131,7 +131,8 @@ typedef struct {
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,
  * v3 wait ticks), 2 staging task (v0 task, v1 step, v2 tile, v3 start tick, v4 1 if
  * done by a stalled compute workgroup, v5 element offset of its destination in the
- * slot ring, -1 if it did not copy), 3 controller update (v0 R_p, v1 R_s, v2 C_p,
+ * slot ring, -1 if it did not copy), 3 controller update (v0 R_p: unclaimed compute
+ * unit-steps outside the last step group, v1 R_s, v2 C_p,
  * v3 C_s, v4 blocks B, v5 new target), 4 role switch (v0 new role: 0 compute,
  * 1 staging, v1 staging-role count after it). t: tick at which it was written. */
 typedef struct {

@@ -316,7 +316,10 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     else if (opts.initial_staging_wgs > 0)
       init = std::min(opts.initial_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
     else
-      init = eq2_target_host(grid, n_units * (int64_t)n_steps, n_stage_tasks, a.cost_compute0, a.cost_stage0);
+      // As on the device: R_p without the last step group, which follows the last
+      // staging task whatever the split.
+      init = eq2_target_host(grid, n_units * (int64_t)mkra::kGroup * (a.n_groups - 1), n_stage_tasks,
+                             a.cost_compute0, a.cost_stage0);
   }
   a.initial_stagers = init;
   a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;

@@ -198,14 +198,23 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   uint64_t cd = ld32(&a.ctrl->compute_done.v), ct = ld64(&a.ctrl->compute_ticks.v);
   uint64_t sd = ld32(&a.ctrl->stage_done.v),
            stt = ld64(&a.ctrl->stage_ticks.v) + ld64(&a.ctrl->stage_wait_ticks.v);
-  int64_t cp = cd ? (int64_t)(ct / cd) : a.cost_compute0;
-  int64_t cs = sd ? (int64_t)(stt / sd) : a.cost_stage0;
+  // The cost-model priors count as one ring step's tasks of each role (n_units
+  // compute unit-steps, n_tiles staging tiles), so the first few measured tasks (cold
+  // caches, no slot waits yet) do not swing the split.
+  const uint64_t kc = (uint64_t)a.n_units, ks = (uint64_t)a.n_tiles;
+  int64_t cp = (int64_t)((ct + kc * (uint64_t)a.cost_compute0) / (cd + kc));
+  int64_t cs = (int64_t)((stt + ks * (uint64_t)a.cost_stage0) / (sd + ks));
   if (cp < 1) cp = 1;
   if (cs < 1) cs = 1;
-  int n = eq2_target(a.grid, rp, rs, cp, cs);
+  // R_p counts the compute work that can overlap the remaining staging: every task of
+  // the last step group needs that group's staged tiles, so its unit-steps follow the
+  // last staging task whatever the split, and Eq. (2) balances the rest.
+  const int64_t last_group = (int64_t)a.n_units * (a.n_steps - kGroup * (a.n_groups - 1));
+  const int64_t rp2 = rp > last_group ? rp - last_group : 0;
+  int n = eq2_target(a.grid, rp2, rs, cp, cs);
   st32(&a.ctrl->target.v, (uint32_t)(n + 1));
   add32(&a.ctrl->ctrl_updates.v, 1);
-  if (a.trace != nullptr) trace_rec(ap, kTraceController, rp, rs, cp, cs, a.grid, n);
+  if (a.trace != nullptr) trace_rec(ap, kTraceController, rp2, rs, cp, cs, a.grid, n);
 }
 // ------------------------------------------------------------------ waits
 // All waits are bounded: past timeout_ticks they raise MK_E_TIMEOUT, and every wait
