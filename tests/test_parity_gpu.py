@@ -280,8 +280,13 @@ def test_stats_and_controller_follow_eq2():
     stage = [r for r in recs if r[2] == 2]
     assert len(comp) == st["compute_tasks_done"] and len(stage) == st["staging_tasks_done"]
     assert len(ctrl) == st["controller_updates"] and len(ctrl) >= 1
+    # R_p as Eq. (2) takes it: unclaimed unit-steps outside the last step group (those
+    # follow the last staging task whatever the split).
+    n_groups = (st["n_steps"] + 1) // 2
+    rp_max = st["n_units"] * 2 * (n_groups - 1)
     for r in ctrl:
         rp, rs, cp, cs, b, target = r[3:9]
+        assert 0 <= rp <= rp_max, (r, rp_max)
         exact = oracle.controller_target(b, rp, rs, cp, cs)
         # The kernel's integer rounding (half up) and clamp to [1, min(B-1, Rs)].
         if rs <= 0:
