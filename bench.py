@@ -122,7 +122,7 @@ def write_traffic(cfg, pmc_dir, copy_mib):
 
 def staging_summary(cfg, stats, ms):
     """The staging role's traffic: every step's chunk read once from its home and
-    written once into the double buffer, in tiles of 128 rows."""
+    written once into the slot ring, in tiles of 128 rows."""
     chunk = 2 * cfg.lk * cfg.hkv * cfg.d * 2
     moved = 2 * cfg.n_steps * chunk  # read + write
     busy_s = stats["staging_busy_ticks"] * 1e-8

@@ -144,7 +144,7 @@ struct KernelArgs {
   int xcd_unit_begin[kMaxXcd + 1];
 
   // Staging work: tasks = (step 0..S-1) x (128-row tile); each step's chunk is staged
-  // into slot step % 2 as blocks of 64 keys per KV head.
+  // into slot step % kSlots as blocks of 64 keys per KV head.
   int n_tiles;            // ceil(Lk / 128)
   int n_blocks;           // 2 * n_tiles: blocks per KV head (keys past Lk staged as zeros)
   int n_stage_tasks;
