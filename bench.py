@@ -244,47 +244,104 @@ def run_probes(rounds=3):
     return "\n".join(out)
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "the host CPU"
+
+
+def oracle_timed(cfg, q, kv, rows):
+    """One timed pass of the fp64 oracle over `rows` (None: every row) of a workload,
+    all heads: the oracle's own function, called once per KV head (a complete problem
+    of its own), the KV heads spread over the cores of this process's affinity mask,
+    BLAS at one thread each. Returns (seconds, algorithmic FLOPs covered, cores)."""
+    import numpy as np
+
+    import oracle
+    from ring_inputs import to_f64
+    from tests.parity import oracle_rows
+
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, cfg.hkv))
+    q64, kv64 = to_f64(q), to_f64(kv)
+    rr = np.arange(cfg.lq) if rows is None else np.asarray(rows)
+    t0 = time.perf_counter()
+    oracle_rows(oracle, q64, kv64, cfg.rank, cfg.causal, cfg.gqa_ratio, rr, workers=workers)
+    dt = time.perf_counter() - t0
+    if cfg.causal:
+        pairs = int(sum(cfg.rank * cfg.lk + int(r) + 1 for r in rr))
+    else:
+        pairs = len(rr) * cfg.n_chunks * cfg.lk
+    return dt, 4 * cfg.d * cfg.hq * pairs, workers
+
+
 def cpu_baseline(cfg, q, kv, budget_rows):
     """The fp64 oracle on the host cores, on a bounded sample of the same workload:
     `budget_rows` query rows spread over the chunk, all heads, all keys."""
     import numpy as np
 
-    import oracle
-    from ring_inputs import to_f64
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
     rows = np.linspace(0, cfg.lq - 1, budget_rows).astype(np.int64)
-    q64, kv64 = to_f64(q), to_f64(kv)
-    t0 = time.perf_counter()
-    oracle.ring_attention_rows(q64, kv64, cfg.rank, cfg.causal, cfg.gqa_ratio, rows)
-    dt = time.perf_counter() - t0
-    if cfg.causal:
-        pairs = sum(cfg.rank * cfg.lk + int(r) + 1 for r in rows)
-    else:
-        pairs = len(rows) * cfg.n_chunks * cfg.lk
-    flops = 4 * cfg.d * cfg.hq * pairs
-    cpu = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    dt, flops, workers = oracle_timed(cfg, q, kv, rows)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
         "sample": f"{len(rows)} of {cfg.lq} query rows (evenly spaced), all {cfg.hq} heads, all visible keys; "
-                  f"{dt:.1f} s on {threads} threads of {cpu or 'the host CPU'}; fp64 NumPy/BLAS, dense over "
-                  f"masked keys too (FLOPs counted for visible pairs only)",
+                  f"{dt:.1f} s on {workers} threads (one KV head per call, BLAS at one thread each; "
+                  f"{len(os.sched_getaffinity(0))} cores in the affinity mask) of {_cpu_model()}; fp64 NumPy, "
+                  f"dense over masked keys too (FLOPs counted for visible pairs only)",
     }
+
+
+def cpu_all_workloads():
+    """One timed oracle pass per workload (every query row, all heads), on the host
+    cores. Returns markdown."""
+    from ring_inputs import CONFIGS, make_inputs
+
+    lines = [f"Host: {_cpu_model()}, {len(os.sched_getaffinity(0))} cores in the affinity mask.", "",
+             "| workload | rows | seconds | threads | algorithmic GFLOP/s |", "|---|---:|---:|---:|---:|"]
+    for i, cfg in enumerate(CONFIGS):
+        q, kv = make_inputs(cfg, seed=i)
+        dt, flops, workers = oracle_timed(cfg, q, kv, None)
+        log(f"[cpu] {cfg.name}: {dt:.1f} s, {flops / dt / 1e9:.1f} GFLOP/s on {workers} threads")
+        lines.append(f"| {cfg.name} | {cfg.lq} | {dt:.2f} | {workers} | {flops / dt / 1e9:.1f} |")
+        del q, kv
+    return "\n".join(lines)
+
+
+def kernel_stats_from(trace_dir, warmup, steps, kernel="ring_attn_kernel"):
+    """Durations of the timed dispatches of the ring kernel in a rocprofv3
+    --kernel-trace run of `bench.py --steps K --warmup W`: the ring kernel's dispatches
+    in order are W warm-ups, then the K timed ones, then the statistics call; only the
+    K timed ones are summarised. Returns markdown."""
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        rows += [r for r in csv.DictReader(open(f)) if kernel in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"no {kernel} dispatches in a *kernel_trace.csv under {trace_dir}")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6 for r in rows]
+    if len(dur) < warmup + steps:
+        raise SystemExit(f"{len(dur)} dispatches, expected at least {warmup + steps}")
+    timed = dur[warmup:warmup + steps]
+    st = sorted(timed)
+    med = statistics.median(timed)
+    span = (int(rows[warmup + steps - 1]["End_Timestamp"]) - int(rows[warmup]["Start_Timestamp"])) * 1e-6
+    return "\n".join([
+        f"Kernel `{rows[0]['Kernel_Name']}`: {len(dur)} dispatches; dispatches {warmup}..{warmup + steps - 1} "
+        f"are the {steps} timed launches.", "",
+        "| timed dispatches | median ms | mean ms | min ms | max ms | first start to last end, ms per launch |",
+        "|---:|---:|---:|---:|---:|---:|",
+        f"| {steps} | {med:.4f} | {sum(timed) / steps:.4f} | {st[0]:.4f} | {st[-1]:.4f} | {span / steps:.4f} |",
+        "", "All dispatches (ms): " + ", ".join(f"{d:.3f}" for d in dur)])
 
 
 def main():
@@ -309,9 +366,20 @@ def main():
                          "profiles/traffic_<workload>.json")
     ap.add_argument("--probes", action="store_true",
                     help="run the MFMA-stream and vector-ALU probes instead of the benchmark; prints markdown")
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="no GPU: one timed oracle pass (every row) per workload on the host cores; prints markdown")
+    ap.add_argument("--kernel-stats-from", default=None,
+                    help="no GPU: summarise the timed dispatches (after --warmup, --steps of them) of a rocprofv3 "
+                         "--kernel-trace run under DIR; prints markdown")
     args = ap.parse_args()
     if args.probes:
         print(run_probes(), flush=True)
+        return
+    if args.cpu_all:
+        print(cpu_all_workloads(), flush=True)
+        return
+    if args.kernel_stats_from:
+        print(kernel_stats_from(args.kernel_stats_from, args.warmup, args.steps), flush=True)
         return
     if args.traffic_from:
         from ring_inputs import CONFIGS, CONFIG_BY_NAME
@@ -426,7 +494,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 QK / fp16 PV",
         "data": "synthetic",
         "config": {
             "workload": cfg.name,

@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
   MK_OK = 0,
   MK_E_INVAL = 1,        /* bad argument: null pointer, shape, dtype, stride, rank, alignment */
-  MK_E_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (head_dim) */
+  MK_E_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (head_dim on the
+                            host; a V value outside the fp16 range, found on the GPU) */
   MK_E_HIP = 3,          /* a HIP runtime call failed (allocation, launch, copy) */
   MK_E_TIMEOUT = 4       /* a bounded on-GPU wait expired; the kernel exited early */
 } mk_status;
@@ -90,15 +91,20 @@ typedef struct {
                                   workgroup reads back the K part of every block it
                                   wrote and compares it with the chunk's home copy;
                                   mismatches are counted in
-                                  mk_ring_attn_stats.debug_mismatches. Other bits are
-                                  ignored. */
+                                  mk_ring_attn_stats.debug_mismatches. bit 1: before
+                                  the launch the host synchronises the stream and
+                                  writes into every ready flag and unit flag of the
+                                  workspace a stamp of the right step but of the
+                                  previous or the next launch, which the kernel must
+                                  not consume. Other bits are ignored. */
   int32_t reserved[5];
 } mk_ring_attn_opts;
 
 /* Filled by mk_ring_attn_fwd_ex when stats != NULL (the call then synchronises the
  * stream). Times are in s_memrealtime ticks (100 MHz). */
 typedef struct {
-  int32_t status;              /* device-side result of the launch (MK_OK / MK_E_TIMEOUT) */
+  int32_t status;              /* device-side result of the launch (MK_OK, MK_E_TIMEOUT, or
+                                  MK_E_UNSUPPORTED for a V outside the fp16 range) */
   int32_t grid_wgs;            /* persistent workgroups launched */
   int32_t n_units;             /* compute units per step (head group x query block) */
   int32_t n_steps;             /* ring steps run */
@@ -164,12 +170,20 @@ typedef struct {
  *  stream     HIP stream the kernel is enqueued on (0 = null stream).
  *
  * Step t (t = 0..S-1) consumes chunk (rank - t) mod N; S = rank+1 if causal, else N.
+ * Precision: QK^T takes Q and K in bf16; the PV product takes V converted to fp16
+ * and P rounded to fp16 (fp32 accumulation throughout). V must therefore satisfy
+ * |v| < 65536 and be finite in every chunk the call reads (chunks after the rank
+ * are not read when causal); a V outside that range is detected by the staging role
+ * on the GPU, ends the launch early (every workgroup exits normally; out and lse are
+ * then undefined) and is reported as MK_E_UNSUPPORTED by mk_ring_attn_status() and
+ * in mk_ring_attn_stats.status. V values below 2^-14 in magnitude are rounded to the
+ * fp16 subnormal grid (absolute error at most 2^-25).
  * D must be 64 or 128 (else MK_E_UNSUPPORTED). Lq, Lk, Hq, Hkv may be any size
  * (ragged tiles are masked); Lq == 0 or Hq == 0 is a no-op returning MK_OK; Lk == 0
  * with Lq > 0 is MK_E_INVAL. Data pointers of non-empty tensors must be 16-byte
  * aligned; out and lse must not overlap the inputs or each other.
- * Asynchronous: returns after enqueueing; a device-side timeout is reported by
- * mk_ring_attn_status(). Results are bitwise reproducible across launches, grid
+ * Asynchronous: returns after enqueueing; device-side errors (an expired wait, a V
+ * out of range) are reported by mk_ring_attn_status(). Results are bitwise reproducible across launches, grid
  * sizes and staging splits (each output is reduced in a fixed order). */
 mk_status mk_ring_attn_fwd(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank, int causal,
                            int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream);
@@ -184,8 +198,10 @@ mk_status mk_ring_attn_fwd_ex(const mk_tensor* q, const mk_tensor* kv_chunks, in
 void mk_ring_attn_default_opts(mk_ring_attn_opts* opts);
 
 /* Synchronises `stream` and returns the device-side status of the calls enqueued on
- * it since the last check: MK_E_TIMEOUT if any of them hit a wait bound, else MK_OK
- * (MK_E_HIP if the synchronisation itself fails). Clears the sticky status. */
+ * it since the last check: MK_E_UNSUPPORTED if any of them staged a V outside the
+ * fp16 range (|v| >= 65536 or not finite), else MK_E_TIMEOUT if any hit a wait bound,
+ * else MK_OK (MK_E_HIP if the synchronisation itself fails). Clears the sticky
+ * status. */
 mk_status mk_ring_attn_status(hipStream_t stream);
 
 /* Copies up to `capacity` trace records of the last traced call on `stream` into the

@@ -42,6 +42,17 @@ def _build_one(sources, lib, verbose):
     os.replace(tmp, lib)
 
 
+def device_asm(out_path: str, source: str = SOURCES[0]) -> str:
+    """gfx950 assembly of one HIP source (device code only), for build checks."""
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc()] + flags + ["--cuda-device-only", "-S", source, "-o", out_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("assembling %s failed" % os.path.basename(source))
+    return open(out_path).read()
+
+
 def build(verbose: bool = False) -> str:
     _build_one(SOURCES, LIB, verbose)
     _build_one(PROBES_SOURCES, PROBES_LIB, verbose)

@@ -152,6 +152,21 @@ bool overlaps(const mk_tensor* a, int64_t ea, const mk_tensor* b, int64_t eb) {
   return a0 < b1 && b0 < a1;
 }
 
+// The status a set of device-side error bits reports: a V outside the fp16 range of
+// the PV operand first (the launch ended because of it), then an expired wait.
+mk_status device_status(uint32_t bits) {
+  if (bits & mkra::kErrRange) return MK_E_UNSUPPORTED;
+  if (bits & mkra::kErrTimeout) return MK_E_TIMEOUT;
+  return bits != 0 ? MK_E_HIP : MK_OK;
+}
+
+const char* device_message(uint32_t bits) {
+  if (bits & mkra::kErrRange)
+    return "a staged V value is outside the fp16 range of the PV operand (|v| >= 65536 or not finite); "
+           "the call's outputs are undefined (status of an earlier call on this stream)";
+  return "a bounded wait on the GPU expired (status of an earlier call on this stream)";
+}
+
 // Same integer Eq. (2) as the kernel's controller.
 int eq2_target_host(int64_t b, int64_t rp, int64_t rs, int64_t cp, int64_t cs) {
   if (rs <= 0) return 0;
@@ -363,6 +378,24 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   w->traced_last = opts.trace != 0;
   a.epoch = ++w->epoch;
 
+  if (opts.debug_flags & 2) {
+    // Debug: every ready flag of the slot ring and every unit flag holds, before the
+    // launch, a stamp of the right step but of the previous or the next launch (even
+    // and odd entries). The kernel must consume none of them.
+    auto stamp = [](uint64_t ep, int step) { return (ep << 20) | (uint64_t)(step + 1); };
+    std::vector<uint64_t> sf((size_t)mkra::kSlots * a.n_tiles), uf((size_t)n_units);
+    for (int sl = 0; sl < mkra::kSlots; ++sl)
+      for (int j = 0; j < a.n_tiles; ++j)
+        sf[(size_t)sl * a.n_tiles + j] = stamp(((sl + j) & 1) ? a.epoch + 1 : a.epoch - 1, sl);
+    for (int64_t u = 0; u < n_units; ++u)
+      uf[(size_t)u] = stamp((u & 1) ? a.epoch + 1 : a.epoch - 1, (int)(u % n_steps));
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if ((e = hipMemcpy(a.slot_flags, sf.data(), sf.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+    if ((e = hipMemcpy(a.unit_flags, uf.data(), uf.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+  }
+
   if ((e = mkra_kernel_launch(&a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
 
   if (stats != nullptr) {
@@ -371,7 +404,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     if ((e = hipMemcpy(&ds, w->status, sizeof(ds), hipMemcpyDeviceToHost)) != hipSuccess)
       return hip_fail(e, "hipMemcpy");
-    stats->status = (int32_t)ds.last_error;
+    stats->status = (int32_t)device_status(ds.last_error);
     stats->grid_wgs = grid;
     stats->n_units = a.n_units;
     stats->n_steps = n_steps;
@@ -435,7 +468,7 @@ mk_status mk_ring_attn_status(hipStream_t stream) {
   const uint32_t zero = 0;
   if ((e = hipMemcpy(&w->status->sticky_error, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
     return hip_fail(e, "hipMemcpy");
-  return fail(MK_E_TIMEOUT, "a bounded wait on the GPU expired (status of an earlier call on this stream)");
+  return fail(device_status(sticky), device_message(sticky));
 }
 
 mk_status mk_ring_attn_trace(hipStream_t stream, mk_trace_record* records, int64_t capacity, int64_t* n_copied) {

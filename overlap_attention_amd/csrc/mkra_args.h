@@ -52,7 +52,9 @@ struct Block {
 };
 
 enum : uint32_t { kRoleCompute = 0, kRoleStage = 1 };
-enum : uint32_t { kErrNone = 0, kErrTimeout = 4 };
+// Device-side errors, one bit each (the host ORs them over launches): a bounded wait
+// expired; a V value outside the fp16 range of the PV operand was staged.
+enum : uint32_t { kErrNone = 0, kErrTimeout = 4, kErrRange = 8 };
 enum : int32_t { kTraceCompute = 1, kTraceStage = 2, kTraceController = 3, kTraceRole = 4 };
 
 // One counter per 64-byte line: the counters are hit by atomics from every CU.

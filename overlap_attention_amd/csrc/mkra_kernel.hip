@@ -53,11 +53,14 @@ enum : int32_t { kOpExit = 0, kOpCompute = 1, kOpStage = 2 };
 __device__ __forceinline__ uint64_t ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 // The launch arguments where the dispatcher placed them (the kernarg segment, where
-// the by-value KernelArgs parameter is the first argument). Out-of-line functions
-// read them through this pointer, so the by-value parameter is never address-taken
-// and never copied to scratch memory.
-// Valid only in the kernel's own body (in a called function the intrinsic has no
-// segment to return): out-of-line functions receive the pointer as an argument.
+// the by-value KernelArgs parameter is the first argument). Functions that may be
+// called out of line read them through this pointer, so the by-value parameter is
+// never address-taken and never copied to scratch memory.
+// Valid only in the kernel's own body: in a function the compiler does not inline,
+// the intrinsic has no segment and yields a null base, and every argument read
+// through it faults. ring_attn_kernel evaluates it once, first thing, and passes the
+// pointer down; nothing else may call it (a build test checks that the only call in
+// the kernels' code is to trace_rec).
 __device__ __forceinline__ const KernelArgs* kernel_args() {
   return (const KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
 }
@@ -343,10 +346,20 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) | (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// Exact bf16 -> fp16 for |v| < 65520 (the fp16 range); two values per 32-bit word.
+// bf16 -> fp16 (round to nearest even), two values per 32-bit word. Exact for
+// 2^-14 <= |v| < 2^16 (fp16 normals hold bf16's 8 significant bits); below 2^-14
+// the fp16 subnormal spacing 2^-24 rounds the value (absolute error at most 2^-25),
+// and |v| >= 2^16 would overflow: the staging role refuses such a V
+// (bf16x2_outside_f16) instead of converting it.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   f16x2 h = {(_Float16)__builtin_bit_cast(float, w << 16), (_Float16)__builtin_bit_cast(float, w & 0xffff0000u)};
   return __builtin_bit_cast(uint32_t, h);
+}
+
+// True if either bf16 of the word has |v| >= 2^16 or is not finite (exponent field
+// >= 127 + 16): a value the fp16 PV operand cannot hold.
+__device__ __forceinline__ bool bf16x2_outside_f16(uint32_t w) {
+  return (w & 0x7f80u) >= (143u << 7) || (w & 0x7f800000u) >= (143u << 23);
 }
 
 // Waits until at most n vector-memory operations of this wave are outstanding.
@@ -386,9 +399,9 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
   uint64_t w = 0;
   // Slot release (every wave waits; a timeout leaves the error word set for all).
   if (t >= kSlots) wave_wait_ge32(a, &a.done_count[t - kSlots], (uint32_t)a.n_units, w);
-  __syncthreads();
-  const bool ok = !has_error(a);
-  __syncthreads();
+  // One verdict for the whole workgroup (the barriers below are inside the branch).
+  const bool ok = __syncthreads_or(has_error(a) ? 1 : 0) == 0;
+  bool v_range = false;  // some V of the tile does not fit the fp16 PV operand
   if (ok) {
     const int c = chunk_of_step(a, t);
     const int64_t row_elems = (int64_t)a.hkv * D;
@@ -428,6 +441,7 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
           const int pos = vt_pos(r);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            v_range |= bf16x2_outside_f16(vr[b][i][e]);
             const uint32_t h2 = bf16x2_to_f16x2(vr[b][i][e]);
             sc[(8 * cc + 2 * e) * VPITCH + pos] = (uint16_t)(h2 & 0xffffu);
             sc[(8 * cc + 2 * e + 1) * VPITCH + pos] = (uint16_t)(h2 >> 16);
@@ -453,6 +467,10 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
       }
       __syncthreads();
     }
+    // A V outside the fp16 range ends the launch through the error path (every wait
+    // returns once the error word is set) and is reported as unsupported.
+    v_range = __syncthreads_or(v_range ? 1 : 0) != 0;
+    if (v_range && tid == 0) raise_error(a, kErrRange);
     if (a.debug_flags & 1) {
       // Debug: re-derive the K part of every block of the tile from the chunk's home.
       uint32_t bad = 0;
@@ -481,7 +499,7 @@ __device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0) {
-    if (ok) st64_release(&a.slot_flags[slot * a.n_tiles + j], stamp(a.epoch, t));
+    if (ok && !v_range) st64_release(&a.slot_flags[slot * a.n_tiles + j], stamp(a.epoch, t));
     const uint64_t busy = ticks() - t_begin - w;
     add64(&a.ctrl->stage_ticks.v, busy);
     add32(&a.ctrl->stage_done.v, 1);
@@ -1279,6 +1297,8 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
+  // The one evaluation of kernel_args(): in the kernel's own body, where it is valid.
+  const KernelArgs* const ap = kernel_args();
   const int tid = threadIdx.x;
   const uint64_t t_start = ticks();
   const uint64_t c_start = __builtin_readcyclecounter();  // s_memtime: shader clock
@@ -1312,7 +1332,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   bool claimed = false;  // the compute task that just ended already claimed the next one
   while (true) {
     __syncthreads();
-    if (!claimed && tid < 64) schedule(kernel_args(), &sched, g_cmd);
+    if (!claimed && tid < 64) schedule(ap, &sched, g_cmd);
     claimed = false;
     __syncthreads();
     const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
@@ -1321,7 +1341,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       const uint64_t t0 = ticks();
       uint64_t w0 = 0;
       compute_task<D>(a, x, y, grp, w0, [&]() {
-        if (tid >= 64 && tid < 128) schedule(kernel_args(), &sched, g_cmd);
+        if (tid >= 64 && tid < 128) schedule(ap, &sched, g_cmd);
       });
       claimed = true;
       if (tid == 0) {
@@ -1332,10 +1352,10 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
         add64(&a.ctrl->compute_wait_ticks.v, w0);
         if (a.trace != nullptr)
           for (int t = t_first; t < t_end; ++t)
-            trace_rec(kernel_args(), kTraceCompute, x, t, (int64_t)t0, (int64_t)w0, 0, 0);
+            trace_rec(ap, kTraceCompute, x, t, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
-      stage_tile<D>(a, kernel_args(), (uint32_t)x, y != 0);
+      stage_tile<D>(a, ap, (uint32_t)x, y != 0);
     }
   }
 

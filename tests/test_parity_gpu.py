@@ -12,7 +12,7 @@ import torch
 import oracle
 import overlap_attention_amd as mk
 from ring_inputs import CONFIGS, RingConfig, make_inputs, to_f64
-from tests.parity import compare, fmt, sample_rows
+from tests.parity import compare, fmt, oracle_rows, wave_slice_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,25 +84,45 @@ def test_small_workload_full():
     check_full(CONFIGS[1], seed=1)
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4], ids=lambda i: CONFIGS[i].name)
-def test_full_size_workloads_sampled(idx):
-    """Full shapes in the default launch configuration (as benchmarked); the oracle
-    evaluates sampled query rows of every head."""
+def check_full_size(idx, rows, label):
+    """A full-size workload in the default launch configuration (as benchmarked),
+    compared with the oracle at `rows` (None: every row), all heads."""
     cfg = CONFIGS[idx]
-    announce(f"{cfg} seed={idx} sampled")
+    announce(f"{cfg} seed={idx} {label}")
     q, kv = make_inputs(cfg, seed=idx)
     qg, kvg = q.cuda(), kv.cuda()
     out, lse, stats = run_gpu(qg, kvg, cfg, want_stats=True)
     print("    stats:", stats, flush=True)
-    rows = sample_rows(cfg.lq, n_random=24, seed=idx)
-    ref_o, ref_l = oracle.ring_attention_rows(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio, rows)
-    rep = compare(to_f64(out[rows]), lse[:, rows].double().cpu().numpy(), ref_o, ref_l)
-    print("   ", fmt(rep), flush=True)
-    assert rep["ok"], fmt(rep)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     assert stats["status"] == 0
     assert stats["compute_tasks_done"] == stats["n_units"] * stats["n_steps"]
     assert stats["staging_tasks_done"] == stats["n_stage_tasks"]
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    out_c, lse_c = out.cpu(), lse.cpu()
+    del qg, kvg, out, lse
+    sel = slice(None) if rows is None else rows
+    print(f"    oracle on {cfg.lq if rows is None else len(rows)} of {cfg.lq} rows, all {cfg.hq} heads", flush=True)
+    ref_o, ref_l = oracle_rows(oracle, to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio, rows,
+                               progress=True)
+    rep = compare(to_f64(out_c[sel]), lse_c[:, sel].double().numpy(), ref_o, ref_l)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_64k_every_row():
+    check_full_size(2, None, "every row")
+
+
+@pytest.mark.timeout(600)
+def test_full_size_128k_every_wave_slice():
+    cfg = CONFIGS[3]
+    check_full_size(3, wave_slice_rows(cfg.lq, per_slice_random=1, seed=3), "first, last and one random row of "
+                    "every 32-row slice")
+
+
+@pytest.mark.timeout(600)
+def test_full_size_32k_d64_every_row():
+    check_full_size(4, None, "every row")
 
 
 SPLIT_VARIANTS = [
@@ -303,6 +323,48 @@ def test_stats_and_controller_follow_eq2():
         assert seen.get(unit, -1) == step - 1
         seen[unit] = step
     assert len(seen) == st["n_units"]
+
+
+def test_v_outside_fp16_range_reports_unsupported():
+    """The PV product takes V in fp16: a V the fp16 format cannot hold (|v| >= 65536 or
+    not finite) in a chunk the call reads ends the launch through the error path and is
+    reported as MK_E_UNSUPPORTED; the next call on the same workspace runs normally."""
+    cfg = shape("vrange", 4, 3, 256, 256, 4, 2, 128, True)
+    q, kv = make_inputs(cfg, seed=8)
+    for where, val in (((1, 1, 77, 1, 5), 1e5), ((3, 1, 200, 0, 100), float("nan")),
+                       ((0, 1, 3, 1, 0), float("-inf"))):
+        bad = kv.clone()
+        bad[where] = val
+        announce(f"V[{where}] = {val}")
+        out, lse, st = mk.ring_attn_fwd(q.cuda(), bad.cuda(), cfg.rank, cfg.causal, cfg.gqa_ratio,
+                                        opts=opts(), want_stats=True)
+        assert st["status"] == mk.MK_E_UNSUPPORTED, st
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_ring_attn_status()
+        assert e.value.status == mk.MK_E_UNSUPPORTED
+        announce("next call on the same workspace")
+        check_full(cfg, seed=8)
+
+
+def test_host_written_stale_and_future_flags_are_not_consumed():
+    """Every ready flag and unit flag holds, before the launch, a stamp of the right
+    step but of the previous or the next launch; the slots hold an earlier launch's
+    data; staging is slow. A consumed flag would read that data."""
+    cfg = shape("flagtable", 6, 5, 256, 256, 8, 4, 128, True)
+    qx, kvx = make_inputs(cfg, seed=33)
+    qy, kvy = make_inputs(cfg, seed=34)
+    ref = oracle.ring_attention_reference(to_f64(qy), to_f64(kvy), cfg.rank, cfg.causal, cfg.gqa_ratio)
+    qx, kvx, qy, kvy = qx.cuda(), kvx.cuda(), qy.cuda(), kvy.cuda()
+    announce("host-written stale and future flags")
+    mk.ring_attn_fwd(qx, kvx, cfg.rank, cfg.causal, cfg.gqa_ratio, opts=opts())
+    out, lse = mk.ring_attn_fwd(qy, kvy, cfg.rank, cfg.causal, cfg.gqa_ratio,
+                                opts=opts(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+                                          stage_delay_ticks=20000, debug_flags=2))
+    torch.cuda.synchronize()
+    mk.mk_ring_attn_status()
+    rep = compare(to_f64(out), lse.double().cpu().numpy(), *ref)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
 
 
 def test_host_pointer_rejected():
