@@ -194,6 +194,26 @@ mk_status mk_ring_attn_fwd_ex(const mk_tensor* q, const mk_tensor* kv_chunks, in
                               int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream,
                               const mk_ring_attn_opts* opts, mk_ring_attn_stats* stats);
 
+/* As mk_ring_attn_fwd (default options), for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It calls no hipMalloc, hipFree or other allocating routine. All of its
+ * device state (control block, flags, the eight-slot KV ring, the fp32 running state)
+ * lives in a fixed array of MKRA_NOALLOC_SCRATCH_BYTES (256 MiB) in the library's
+ * code object, one per GPU, held from the library's first use on that GPU until the
+ * process ends. A problem whose state does not fit (about 8 staged copies of one KV
+ * chunk plus 17 KB of fp32 state per 32 query rows and head, e.g. the 64K-token GQA
+ * rank share fits, a 128K-token one does not) returns MK_E_UNSUPPORTED before
+ * anything is enqueued. Each call first clears the control block, counters and flags
+ * of the array with a small kernel on `stream` (no memset), then launches the ring
+ * kernel. Every call on a GPU shares that GPU's array and it keeps the last call's
+ * contents: calls that overlap on one GPU (different streams, or different threads
+ * without ordering) race and must not be issued. Device-side errors of these calls
+ * are reported by mk_ring_attn_status() on any stream of the same device. */
+mk_status mk_ring_attn_fwd_noalloc(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank,
+                                   int causal, int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream);
+
+#define MKRA_NOALLOC_SCRATCH_BYTES (256ull << 20)
+
 /* Fills *opts with the defaults (adaptive split, all CUs, 10 s wait bound). */
 void mk_ring_attn_default_opts(mk_ring_attn_opts* opts);
 

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     mk_release_workspace,
     mk_ring_attn_fwd,
     mk_ring_attn_fwd_ex,
+    mk_ring_attn_fwd_noalloc,
     mk_ring_attn_status,
     mk_ring_attn_trace,
     ring_attn_fwd,

@@ -92,6 +92,9 @@ _PROTOTYPES = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(mk_tensor),
                                            ctypes.POINTER(mk_tensor), ctypes.c_void_p,
                                            ctypes.POINTER(mk_ring_attn_opts), ctypes.POINTER(mk_ring_attn_stats)]),
+    "mk_ring_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(mk_tensor), ctypes.POINTER(mk_tensor), ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(mk_tensor),
+                                                ctypes.POINTER(mk_tensor), ctypes.c_void_p]),
     "mk_ring_attn_default_opts": (None, [ctypes.POINTER(mk_ring_attn_opts)]),
     "mk_ring_attn_status": (ctypes.c_int, [ctypes.c_void_p]),
     "mk_ring_attn_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(mk_trace_record), ctypes.c_int64,
@@ -185,6 +188,16 @@ def mk_ring_attn_fwd_ex(q, kv_chunks, n_chunks: int, rank: int, causal: bool, gq
                                    ctypes.byref(opts) if opts is not None else None,
                                    ctypes.byref(st) if st is not None else None))
     return st.as_dict() if st is not None else None
+
+
+def mk_ring_attn_fwd_noalloc(q, kv_chunks, n_chunks: int, rank: int, causal: bool, gqa_ratio: int, out, lse,
+                             stream=None) -> None:
+    """Thin call of mk_ring_attn_fwd_noalloc (the entry point that allocates no device
+    memory) on torch tensors the caller allocated."""
+    lib = load_library()
+    qd, kd, od, ld = tensor_desc(q), tensor_desc(kv_chunks), tensor_desc(out), tensor_desc(lse)
+    _check(lib.mk_ring_attn_fwd_noalloc(ctypes.byref(qd), ctypes.byref(kd), n_chunks, rank, int(bool(causal)),
+                                        gqa_ratio, ctypes.byref(od), ctypes.byref(ld), _stream_ptr(stream)))
 
 
 def mk_ring_attn_status(stream=None) -> int:

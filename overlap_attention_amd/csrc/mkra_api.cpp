@@ -19,6 +19,11 @@
 extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_kernel_launch(const mkra::KernelArgs* a,
                                                                               hipStream_t stream);
 extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_kernel_occupancy(int d, int* blocks_per_cu);
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_scratch_address(int device, void** ptr);
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_zero_launch(void* p, uint64_t bytes,
+                                                                            hipStream_t stream);
+
+static_assert(mkra::kScratchBytes == MKRA_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
 
 namespace {
 
@@ -60,6 +65,16 @@ struct Workspace {
 
 std::mutex g_mu;
 std::vector<Workspace*> g_ws;
+
+// State of the entry point that allocates nothing, per device: whether its scratch
+// array has been set up (status word cleared) and the epoch of its last launch.
+struct ScratchState {
+  bool ready = false;
+  uint64_t epoch = 0;
+};
+std::vector<ScratchState> g_scratch;
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct DeviceInfo {
   int cus = 0;
@@ -216,8 +231,12 @@ mk_status check_device_pointer(const void* p, int dev, const char* name) {
   return MK_OK;
 }
 
+// no_alloc: take every piece of device state from the fixed scratch array of the
+// current device instead of the per-(device, stream) workspace, and call nothing that
+// allocates device memory.
 mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, int causal, int gqa, mk_tensor* out,
-              mk_tensor* lse, hipStream_t stream, const mk_ring_attn_opts* user_opts, mk_ring_attn_stats* stats) {
+              mk_tensor* lse, hipStream_t stream, const mk_ring_attn_opts* user_opts, mk_ring_attn_stats* stats,
+              bool no_alloc = false) {
   g_last_error.clear();
   mk_ring_attn_opts opts;
   mk_ring_attn_default_opts(&opts);
@@ -340,6 +359,49 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;
   a.ctrl_period_ticks = (uint64_t)(opts.controller_period_us > 0 ? opts.controller_period_us : 20) * 100ull;
 
+  if (no_alloc) {
+    // Layout of the scratch array: [status | control block | done counts | slot flags |
+    // unit flags | slot ring + discard block | running state], each part 256-aligned.
+    const uint64_t o_ctrl = align256(sizeof(DevStatus));
+    const uint64_t o_done = o_ctrl + align256(sizeof(DevCtrl));
+    const uint64_t o_sflags = o_done + align256((uint64_t)n_steps * sizeof(uint32_t));
+    const uint64_t o_uflags = o_sflags + align256((uint64_t)mkra::kSlots * a.n_tiles * sizeof(uint64_t));
+    const uint64_t o_slots = o_uflags + align256((uint64_t)n_units * sizeof(uint64_t));
+    const uint64_t o_acc = o_slots + align256((uint64_t)mkra::kSlots * a.slot_bytes + mkra::kDiscardBytes);
+    const uint64_t need =
+        o_acc + (n_steps > 1 ? (uint64_t)n_units * mkra::kWaves * (32 * d + 256) * sizeof(float) : 0);
+    if (need > mkra::kScratchBytes)
+      return fail(MK_E_UNSUPPORTED, "this problem needs " + std::to_string(need) +
+                                        " bytes of device state; the no-allocation entry point holds " +
+                                        std::to_string(mkra::kScratchBytes));
+    void* base = nullptr;
+    if ((e = mkra_scratch_address(dev, &base)) != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    uint8_t* b = static_cast<uint8_t*>(base);
+    if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1);
+    ScratchState& ss = g_scratch[dev];
+    // The status word survives launches (it is cleared by mk_ring_attn_status); the
+    // control block, counters and flags start at zero on every call, so a call never
+    // sees a flag of an earlier one whatever its epoch.
+    if (!ss.ready) {
+      if ((e = mkra_zero_launch(b, o_ctrl, stream)) != hipSuccess) return hip_fail(e, "scratch clear");
+      ss.ready = true;
+    }
+    if ((e = mkra_zero_launch(b + o_ctrl, o_slots - o_ctrl, stream)) != hipSuccess)
+      return hip_fail(e, "scratch clear");
+    a.status = reinterpret_cast<DevStatus*>(b);
+    a.ctrl = reinterpret_cast<DevCtrl*>(b + o_ctrl);
+    a.done_count = reinterpret_cast<uint32_t*>(b + o_done);
+    a.slot_flags = reinterpret_cast<uint64_t*>(b + o_sflags);
+    a.unit_flags = reinterpret_cast<uint64_t*>(b + o_uflags);
+    a.slots = b + o_slots;
+    a.acc = n_steps > 1 ? reinterpret_cast<float*>(b + o_acc) : nullptr;
+    a.trace = nullptr;
+    a.trace_cap = 0;
+    a.epoch = ++ss.epoch;
+    if ((e = mkra_kernel_launch(&a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+    return MK_OK;
+  }
+
   Workspace* w = find_ws(dev, stream, true);
 #define GROW(field, cap, need, zero)                                                   \
   if ((e = grow(&w->field, &cap, (size_t)(need), stream, zero)) != hipSuccess) \
@@ -452,6 +514,11 @@ mk_status mk_ring_attn_fwd_ex(const mk_tensor* q, const mk_tensor* kv_chunks, in
   return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, opts, stats);
 }
 
+mk_status mk_ring_attn_fwd_noalloc(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank,
+                                   int causal, int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream) {
+  return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, nullptr, nullptr, true);
+}
+
 mk_status mk_ring_attn_status(hipStream_t stream) {
   g_last_error.clear();
   int dev = 0;
@@ -459,15 +526,29 @@ mk_status mk_ring_attn_status(hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_mu);
   if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  // The stream's workspace, and the device's scratch array of the no-allocation entry
+  // point if it has been used.
+  DevStatus* words[2] = {nullptr, nullptr};
   Workspace* w = find_ws(dev, stream, false);
-  if (w == nullptr || w->status == nullptr) return MK_OK;
+  if (w != nullptr) words[0] = w->status;
+  if ((int)g_scratch.size() > dev && g_scratch[dev].ready) {
+    void* base = nullptr;
+    if ((e = mkra_scratch_address(dev, &base)) != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    words[1] = static_cast<DevStatus*>(base);
+  }
   uint32_t sticky = 0;
-  if ((e = hipMemcpy(&sticky, &w->status->sticky_error, sizeof(sticky), hipMemcpyDeviceToHost)) != hipSuccess)
-    return hip_fail(e, "hipMemcpy");
+  for (DevStatus* st : words) {
+    if (st == nullptr) continue;
+    uint32_t v = 0;
+    if ((e = hipMemcpy(&v, &st->sticky_error, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+    if (v == 0) continue;
+    sticky |= v;
+    const uint32_t zero = 0;
+    if ((e = hipMemcpy(&st->sticky_error, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy");
+  }
   if (sticky == 0) return MK_OK;
-  const uint32_t zero = 0;
-  if ((e = hipMemcpy(&w->status->sticky_error, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
-    return hip_fail(e, "hipMemcpy");
   return fail(device_status(sticky), device_message(sticky));
 }
 

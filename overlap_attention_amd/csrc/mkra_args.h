@@ -35,6 +35,10 @@ static_assert(kSlots >= 2 * kGroup, "a group task may depend only on groups <= g
 // (one block of the largest head dim; the contents are never used).
 constexpr int kDiscardBytes = 2 * kBN * 128 * 2;
 constexpr int kMaxXcd = 8;
+// Size of the fixed per-device scratch array of the entry point that allocates
+// nothing (mk_ring_attn_fwd_noalloc): its control block, flags, slot ring and running
+// state must fit in it.
+constexpr uint64_t kScratchBytes = 256ull << 20;
 
 // A staged KV block: the keys [64*kt, 64*kt + 64) of one KV head, laid out as the
 // compute role's LDS wants them, so a block moves into LDS as one contiguous copy.

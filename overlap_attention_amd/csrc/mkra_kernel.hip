@@ -19,6 +19,7 @@
 // B = P^T straight from registers).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -1407,7 +1408,48 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
 template __global__ void ring_attn_kernel<64>(KernelArgs);
 template __global__ void ring_attn_kernel<128>(KernelArgs);
 
+// ------------------------------------------------------------------ fixed scratch
+
+// Device memory of the entry point that allocates nothing: the control block, the
+// flags, the slot ring and the running state of its launches, laid out by the host.
+// Each GPU the library runs on holds its own copy until the process ends; every call
+// on a GPU shares it. Host code never passes this name to a kernel (on the host it is
+// only a stand-in): it uses the address hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Zeroes n 32-bit words (a kernel rather than a memset, so a caller may capture it in
+// a graph).
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 }  // namespace mkra
+
+// Device address of this device's scratch array, looked up once per device (with that
+// device current) and kept. Called with the library lock held.
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_scratch_address(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (addr[device] == nullptr) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(mkra::scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_zero_launch(void* p, uint64_t bytes,
+                                                                            hipStream_t stream) {
+  const uint64_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<uint64_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(mkra::zero_words, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
 
 // Host-side entry points of this translation unit (used by the C-ABI layer).
 extern "C" __attribute__((visibility("hidden"))) hipError_t mkra_kernel_launch(const mkra::KernelArgs* a,
