@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MKRA_ABI_VERSION 1
+#define MKRA_ABI_VERSION 2
 
 typedef enum {
   MK_OK = 0,
@@ -66,12 +66,22 @@ typedef struct {
   int64_t stride[5];
 } mk_tensor;
 
-typedef enum { MK_SPLIT_ADAPTIVE = 0, MK_SPLIT_FIXED = 1 } mk_split_mode;
+typedef enum { MK_SPLIT_ADAPTIVE = 0, MK_SPLIT_FIXED = 1, MK_SPLIT_ADAPTIVE_PAPER = 2 } mk_split_mode;
 
 typedef struct {
   int32_t split_mode;          /* mk_split_mode. ADAPTIVE (default): the controller of
                                   §3.2 re-targets the staging-workgroup count with
-                                  Eq. (2) from measured per-task costs. FIXED:
+                                  Eq. (2) from measured per-task costs, with two
+                                  changes to its inputs: R_p leaves out the compute
+                                  of the last step group (it can only follow the last
+                                  staging task), and C_p, C_s are averaged with the
+                                  cost model's priors weighted as one ring step (C_s
+                                  counting a staging task's waits for a free slot).
+                                  ADAPTIVE_PAPER: Eq. (2) as §3.2 states it, R_p all
+                                  remaining compute tasks (unit-steps), R_s all
+                                  remaining staging tasks, C_p and C_s the measured
+                                  busy cycles per finished task of each role (the cost
+                                  model only until a role has finished a task). FIXED:
                                   workgroups 0..fixed_staging_wgs-1 stage (by block
                                   index) until staging work runs out, then compute. */
   int32_t fixed_staging_wgs;   /* FIXED mode only: number of staging workgroups. */
@@ -97,7 +107,17 @@ typedef struct {
                                   workspace a stamp of the right step but of the
                                   previous or the next launch, which the kernel must
                                   not consume. Other bits are ignored. */
-  int32_t reserved[5];
+  int32_t steps_per_task;      /* ring steps a compute task runs with the running state
+                                  in registers, 1..4; 0 = the library's default (2 for
+                                  chunks of Lk*D >= 2^19, else 4). */
+  int32_t tail_steps;          /* the last tail_steps ring steps run in tasks of
+                                  tail_steps_per_task steps (shorter tasks shorten the
+                                  end of the launch); 0 = default (4 when tasks have more than two
+                                  steps and the units outnumber the workgroups, else
+                                  none), < 0 = none. */
+  int32_t tail_steps_per_task; /* 1..steps_per_task (larger values are clamped to it);
+                                  0 = default (2). */
+  int32_t reserved[2];
 } mk_ring_attn_opts;
 
 /* Filled by mk_ring_attn_fwd_ex when stats != NULL (the call then synchronises the
@@ -131,14 +151,16 @@ typedef struct {
                                   lifetime, summed */
   int64_t wg_ticks;            /* the same lifetimes in 100 MHz ticks: the average
                                   shader clock is wg_cycles / wg_ticks * 100 MHz */
-  int64_t reserved[1];
+  int32_t steps_per_task;      /* ring steps per compute task in this launch (before
+                                  the tail) */
+  int32_t step_groups;         /* compute tasks per unit */
 } mk_ring_attn_stats;
 
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,
  * v3 wait ticks), 2 staging task (v0 task, v1 step, v2 tile, v3 start tick, v4 1 if
  * done by a stalled compute workgroup, v5 element offset of its destination in the
- * slot ring, -1 if it did not copy), 3 controller update (v0 R_p: unclaimed compute
- * unit-steps outside the last step group, v1 R_s, v2 C_p,
+ * slot ring, -1 if it did not copy), 3 controller update (v0 R_p as Eq. (2) takes it:
+ * unclaimed compute unit-steps, outside the last step group in ADAPTIVE mode, v1 R_s, v2 C_p,
  * v3 C_s, v4 blocks B, v5 new target), 4 role switch (v0 new role: 0 compute,
  * 1 staging, v1 staging-role count after it). t: tick at which it was written. */
 typedef struct {

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     MK_F32,
     MK_OK,
     MK_SPLIT_ADAPTIVE,
+    MK_SPLIT_ADAPTIVE_PAPER,
     MK_SPLIT_FIXED,
     MkError,
     default_opts,

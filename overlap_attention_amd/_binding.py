@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmkra.so")
 MK_OK, MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_HIP, MK_E_TIMEOUT = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "MK_OK", 1: "MK_E_INVAL", 2: "MK_E_UNSUPPORTED", 3: "MK_E_HIP", 4: "MK_E_TIMEOUT"}
 MK_BF16, MK_F32 = 1, 2
-MK_SPLIT_ADAPTIVE, MK_SPLIT_FIXED = 0, 1
+MK_SPLIT_ADAPTIVE, MK_SPLIT_FIXED, MK_SPLIT_ADAPTIVE_PAPER = 0, 1, 2
 
 
 class mk_tensor(ctypes.Structure):
@@ -43,7 +43,10 @@ class mk_ring_attn_opts(ctypes.Structure):
         ("disable_staging", ctypes.c_int32),
         ("stage_delay_ticks", ctypes.c_int32),
         ("debug_flags", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("steps_per_task", ctypes.c_int32),
+        ("tail_steps", ctypes.c_int32),
+        ("tail_steps_per_task", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -72,11 +75,12 @@ class mk_ring_attn_stats(ctypes.Structure):
         ("debug_mismatches", ctypes.c_int64),
         ("wg_cycles", ctypes.c_int64),
         ("wg_ticks", ctypes.c_int64),
-        ("reserved", ctypes.c_int64 * 1),
+        ("steps_per_task", ctypes.c_int32),
+        ("step_groups", ctypes.c_int32),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_ if not name.startswith("reserved")}
 
 
 class mk_trace_record(ctypes.Structure):

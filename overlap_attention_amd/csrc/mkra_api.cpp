@@ -193,6 +193,24 @@ int eq2_target_host(int64_t b, int64_t rp, int64_t rs, int64_t cp, int64_t cs) {
   return (int)std::max(lo, std::min(hi, n));
 }
 
+// Step groups unless the options say otherwise. A task boundary costs about the same
+// whatever the step's size (state store and reload, publish, claim), while a longer
+// task leaves workgroups idle longer at the end of the launch. Measured on MI355X
+// (same-box A/B): steps of Lk*D < 2^19 key-dims (the 32K-token MHA D=64 workload,
+// 1024-token chunks) run best in four-step tasks, 2-9% faster than two-step ones; the
+// 64K-token GQA workload (Lk*D = 2^19) runs best in two-step tasks (0.9% faster than
+// four with a tail), the 128K-token one within 0.5% either way. A tail of shorter tasks
+// (the last kDefaultTailSteps steps in tasks of kDefaultTailStepsPerTask) applies only
+// to four-step tasks when the units outnumber the workgroups.
+constexpr int kDefaultTailStepsPerTask = 2;
+constexpr int kDefaultTailSteps = 4;
+int default_steps_per_task(int64_t lk, int64_t d) { return lk * d >= (int64_t(1) << 19) ? 2 : 4; }
+
+// First step of step group g (as the kernel's group_first).
+int group_first_host(const mkra::KernelArgs& a, int g) {
+  return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group;
+}
+
 // Largest divisor of g that divides the wave count: query heads per unit.
 int heads_per_unit(int g) {
   int best = 1;
@@ -261,8 +279,13 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   if (overlaps(out, 2, q, 2) || overlaps(out, 2, kv, 2) || overlaps(lse, 4, q, 2) || overlaps(lse, 4, kv, 2) ||
       overlaps(lse, 4, out, 2))
     return fail(MK_E_INVAL, "out/lse overlap an input or each other");
-  if (opts.split_mode != MK_SPLIT_ADAPTIVE && opts.split_mode != MK_SPLIT_FIXED)
+  if (opts.split_mode != MK_SPLIT_ADAPTIVE && opts.split_mode != MK_SPLIT_FIXED &&
+      opts.split_mode != MK_SPLIT_ADAPTIVE_PAPER)
     return fail(MK_E_INVAL, "opts.split_mode");
+  if (opts.steps_per_task < 0 || opts.steps_per_task > mkra::kMaxGroup)
+    return fail(MK_E_INVAL, "opts.steps_per_task must be 0 (default) or 1..4");
+  if (opts.tail_steps_per_task < 0 || opts.tail_steps_per_task > mkra::kMaxGroup)
+    return fail(MK_E_INVAL, "opts.tail_steps_per_task must be 0 (default) or 1..4");
   if (opts.fixed_staging_wgs < 0 || opts.initial_staging_wgs < 0 || opts.grid_wgs < 0 || opts.spin_timeout_us < 0 ||
       opts.controller_period_us < 0 || opts.trace_capacity < 0 || opts.stage_delay_ticks < 0)
     return fail(MK_E_INVAL, "negative option");
@@ -285,7 +308,6 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   a.lse = static_cast<float*>(lse->data);
   a.lq = (int)lq; a.lk = (int)lk; a.hq = (int)hq; a.hkv = (int)hkv; a.d = (int)d; a.gqa = gqa;
   a.n_chunks = n_chunks; a.rank = rank; a.causal = causal ? 1 : 0; a.n_steps = n_steps;
-  a.n_groups = (n_steps + mkra::kGroup - 1) / mkra::kGroup;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.hg = heads_per_unit(gqa);
   a.n_hgroups = gqa / a.hg;
@@ -329,6 +351,21 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   a.n_xcd = std::min(mkra::kMaxXcd, grid);
   for (int x = 0; x <= a.n_xcd; ++x) a.xcd_unit_begin[x] = (int)((int64_t)x * n_units / a.n_xcd);
 
+  // Step groups: `group` steps each, except the last tail_steps steps, which run in
+  // groups of tail_group (shorter tasks at the end shorten the launch's tail).
+  a.group = opts.steps_per_task > 0 ? opts.steps_per_task : default_steps_per_task(lk, d);
+  a.tail_group = opts.tail_steps_per_task > 0 ? std::min(opts.tail_steps_per_task, a.group)
+                                              : std::min(kDefaultTailStepsPerTask, a.group);
+  {
+    // By default only a launch whose units outnumber its workgroups (several rounds of
+    // tasks) has a tail; with fewer units every task starts at once.
+    const int tail_default = (a.group > kDefaultTailStepsPerTask && n_units > (int64_t)a.grid) ? kDefaultTailSteps : 0;
+    const int tail_steps = opts.tail_steps > 0 ? opts.tail_steps : opts.tail_steps < 0 ? 0 : tail_default;
+    a.n_big = std::max(0, n_steps - tail_steps) / a.group;
+    const int rest = n_steps - a.n_big * a.group;
+    a.n_groups = a.n_big + (rest + a.tail_group - 1) / a.tail_group;
+  }
+
   // Cost model for the controller's priors and the initial split (Eq. (2) with
   // modelled costs; §3.2: the data dependency sets the initial allocation).
   // Compute: a task's FLOPs at half of one CU's bf16 MFMA peak (4096 FLOP/clk at
@@ -340,6 +377,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   const double tile_bytes = 2.0 * 2.0 * 2.0 * (double)std::min<int64_t>(mkra::kStageRows, lk) * hkv * d;
   a.cost_stage0 = std::max<int64_t>(1, (int64_t)(tile_bytes / 40e9 * 1e8));
   a.split_fixed = opts.split_mode == MK_SPLIT_FIXED ? 1 : 0;
+  a.ctrl_paper = opts.split_mode == MK_SPLIT_ADAPTIVE_PAPER ? 1 : 0;
   a.disable_staging = opts.disable_staging ? 1 : 0;
   a.stage_delay_ticks = opts.stage_delay_ticks;
   a.debug_flags = opts.debug_flags;
@@ -349,10 +387,13 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
       init = std::min(opts.fixed_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
     else if (opts.initial_staging_wgs > 0)
       init = std::min(opts.initial_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
+    else if (a.ctrl_paper)
+      // Eq. (2) as the paper states it: every compute task remains.
+      init = eq2_target_host(grid, n_units * (int64_t)n_steps, n_stage_tasks, a.cost_compute0, a.cost_stage0);
     else
       // As on the device: R_p without the last step group, which follows the last
       // staging task whatever the split.
-      init = eq2_target_host(grid, n_units * (int64_t)mkra::kGroup * (a.n_groups - 1), n_stage_tasks,
+      init = eq2_target_host(grid, n_units * (int64_t)group_first_host(a, a.n_groups - 1), n_stage_tasks,
                              a.cost_compute0, a.cost_stage0);
   }
   a.initial_stagers = init;
@@ -489,6 +530,8 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     stats->debug_mismatches = ds.debug_mismatch;
     stats->wg_cycles = ds.wg_cycles;
     stats->wg_ticks = ds.wg_ticks;
+    stats->steps_per_task = a.group;
+    stats->step_groups = a.n_groups;
   }
   return MK_OK;
 }

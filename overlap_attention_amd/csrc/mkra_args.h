@@ -23,14 +23,15 @@ constexpr int kStages = 4;
 // the staging role run up to three step groups ahead of the slowest unit, so a group's
 // tiles need not all be staged within one group's compute time.
 constexpr int kSlots = 8;
-// Ring steps per compute task: a task runs kGroup consecutive steps of one unit with
-// the running state in registers, so the state is stored and reloaded, and a task
-// claimed, once per kGroup steps. A task of group g needs steps kGroup*g .. staged,
-// which needs every unit past step kGroup*g + kGroup - 1 - kSlots, i.e. group
-// g - kSlots/kGroup complete (g-2 or earlier): one group of claim look-ahead stays
-// deadlock-free.
-constexpr int kGroup = 2;
-static_assert(kSlots >= 2 * kGroup, "a group task may depend only on groups <= g-2");
+// Ring steps per compute task (KernelArgs::group for the first step groups, tail_group
+// for the last ones; at most kMaxGroup): a task runs its group's consecutive steps of
+// one unit with the running state in registers, so the state is stored and reloaded,
+// and a task claimed, once per group. A task of group g needs
+// its steps staged, which needs every unit past step group*(g+1) - 1 - kSlots, i.e.
+// group g - kSlots/group complete (g-2 or earlier while kSlots >= 2*group): one group
+// of claim look-ahead stays deadlock-free.
+constexpr int kMaxGroup = 4;
+static_assert(kSlots >= 2 * kMaxGroup, "a group task may depend only on groups <= g-2");
 // Bytes after the ring slots that the compute role's discarded block copies read
 // (one block of the largest head dim; the contents are never used).
 constexpr int kDiscardBytes = 2 * kBN * 128 * 2;
@@ -136,7 +137,10 @@ struct KernelArgs {
   float* lse;             // [Hq, Lq] fp32
   int lq, lk, hq, hkv, d, gqa;
   int n_chunks, rank, causal, n_steps;
-  int n_groups;           // ceil(n_steps / kGroup): compute tasks per unit
+  int group;              // ring steps of each of the first n_big step groups, 1..kMaxGroup
+  int n_big;              // step groups of `group` steps
+  int tail_group;         // ring steps of each later step group, 1..group
+  int n_groups;           // step groups: compute tasks per unit
   float scale_log2;       // log2(e) / sqrt(D)
 
   // Decomposition into compute units: a unit is (KV head, group of HG query heads
@@ -172,6 +176,7 @@ struct KernelArgs {
   // Scheduling.
   int grid;
   int split_fixed;        // 1 = FIXED split
+  int ctrl_paper;         // 1 = Eq. (2) with the paper's inputs (all remaining tasks, measured costs)
   int initial_stagers;
   int disable_staging;
   int stage_delay_ticks;

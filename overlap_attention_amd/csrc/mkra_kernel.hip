@@ -166,14 +166,26 @@ __device__ __forceinline__ int64_t units_in_queue(const KA& a, int x) {
   return a.xcd_unit_begin[x + 1] - a.xcd_unit_begin[x];
 }
 
+// Step groups: the first n_big groups have `group` steps each, the later ones (the
+// tail) `tail_group` steps each, the last one possibly fewer. First step of group g,
+// and one past its last.
+template <class KA>
+__device__ __forceinline__ int group_first(const KA& a, int g) {
+  return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group;
+}
+template <class KA>
+__device__ __forceinline__ int group_end(const KA& a, int g) {
+  return min(a.n_steps, group_first(a, g + 1));
+}
+
 // Unit-steps covered by the first h tasks of a queue of ux units (tasks are
-// group-major; every group has kGroup steps but possibly the last).
+// group-major).
 template <class KA>
 __device__ __forceinline__ int64_t steps_claimed(const KA& a, int64_t ux, int64_t h) {
   if (h >= ux * a.n_groups) return ux * a.n_steps;
-  const int64_t g = h / ux;
-  const int64_t in_g = min((int64_t)kGroup, (int64_t)a.n_steps - g * kGroup);
-  return ux * g * kGroup + (h % ux) * in_g;
+  const int g = (int)(h / ux);
+  const int f = group_first(a, g);
+  return ux * f + (h % ux) * (group_end(a, g) - f);
 }
 
 // Run by one lane, from a snapshot of the queue heads and the staging head. Compute
@@ -206,15 +218,25 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   // compute unit-steps, n_tiles staging tiles), so the first few measured tasks (cold
   // caches, no slot waits yet) do not swing the split.
   const uint64_t kc = (uint64_t)a.n_units, ks = (uint64_t)a.n_tiles;
-  int64_t cp = (int64_t)((ct + kc * (uint64_t)a.cost_compute0) / (cd + kc));
-  int64_t cs = (int64_t)((stt + ks * (uint64_t)a.cost_stage0) / (sd + ks));
+  int64_t cp, cs, rp2;
+  if (a.ctrl_paper) {
+    // Eq. (2) with the inputs §3.2 names: every remaining task of each role and the
+    // measured busy cost per finished task (the cost model until a role has finished
+    // one).
+    cp = cd > 0 ? (int64_t)(ct / cd) : a.cost_compute0;
+    cs = sd > 0 ? (int64_t)(ld64(&a.ctrl->stage_ticks.v) / sd) : a.cost_stage0;
+    rp2 = rp;
+  } else {
+    cp = (int64_t)((ct + kc * (uint64_t)a.cost_compute0) / (cd + kc));
+    cs = (int64_t)((stt + ks * (uint64_t)a.cost_stage0) / (sd + ks));
+    // R_p counts the compute work that can overlap the remaining staging: every task
+    // of the last step group needs that group's staged tiles, so its unit-steps follow
+    // the last staging task whatever the split, and Eq. (2) balances the rest.
+    const int64_t last_group = (int64_t)a.n_units * (a.n_steps - group_first(a, a.n_groups - 1));
+    rp2 = rp > last_group ? rp - last_group : 0;
+  }
   if (cp < 1) cp = 1;
   if (cs < 1) cs = 1;
-  // R_p counts the compute work that can overlap the remaining staging: every task of
-  // the last step group needs that group's staged tiles, so its unit-steps follow the
-  // last staging task whatever the split, and Eq. (2) balances the rest.
-  const int64_t last_group = (int64_t)a.n_units * (a.n_steps - kGroup * (a.n_groups - 1));
-  const int64_t rp2 = rp > last_group ? rp - last_group : 0;
   int n = eq2_target(a.grid, rp2, rs, cp, cs);
   st32(&a.ctrl->target.v, (uint32_t)(n + 1));
   add32(&a.ctrl->ctrl_updates.v, 1);
@@ -225,7 +247,7 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
 // returns early once any error is raised, so every workgroup reaches its exit.
 
 // Wave-wide wait until *p >= target; acquire on success.
-__device__ bool wave_wait_ge32(const KernelArgs& a, uint32_t* p, uint32_t target, uint64_t& waited) {
+__device__ __forceinline__ bool wave_wait_ge32(const KernelArgs& a, uint32_t* p, uint32_t target, uint64_t& waited) {
   if (ld32(p) >= target) {
     fence_acquire();
     return true;
@@ -244,7 +266,7 @@ __device__ bool wave_wait_ge32(const KernelArgs& a, uint32_t* p, uint32_t target
 
 
 // Wave-wide wait until *p == value (an epoch stamp); acquire on success.
-__device__ bool wave_wait_stamp(const KernelArgs& a, const uint64_t* p, uint64_t value, uint64_t& waited) {
+__device__ __forceinline__ bool wave_wait_stamp(const KernelArgs& a, const uint64_t* p, uint64_t value, uint64_t& waited) {
   if (ld64(p) == value) {
     fence_acquire();
     return true;
@@ -386,7 +408,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 // One release per
 // tile publishes its epoch-stamped flag (paper §4: epoch-stamped readiness flags).
 template <int D>
-__device__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k, bool assist) {
+__device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k, bool assist) {
   constexpr int CPR = D / 8;                        // 16-byte chunks per K/V row
   constexpr int KCH = kBN * CPR / kThreads;         // K (or V) chunks per thread per block
   constexpr int VPITCH = kBN + 2;                   // fp16 scratch row pitch (breaks bank conflicts)
@@ -684,9 +706,33 @@ struct MPhase {
   }
 };
 
+// This wave's slice of the staged blocks of step t for the KV head at head_off (slot of
+// step t: t mod kSlots), in scalar registers.
+template <int D>
+__device__ __forceinline__ const uint8_t* task_slot_ptr(const KernelArgs& a, int t, int64_t head_off) {
+  return wave_bcast_ptr(a.slots + (int64_t)((uint32_t)t % (uint32_t)kSlots) * a.slot_bytes + head_off);
+}
+
+// The ready flags of the tiles of step t.
+__device__ __forceinline__ const uint64_t* step_flags(const KernelArgs& a, int t) {
+  return a.slot_flags + ((uint32_t)t % (uint32_t)kSlots) * a.n_tiles;
+}
+
+// Tile gi of a task's tile sequence (the tiles of its steps in order: nt0 of the first
+// step starting at t_first, ntf of each later one; at most four steps): its flag and
+// the stamp that flag holds once the tile is staged.
+__device__ __forceinline__ void task_tile_flag(const KernelArgs& a, int t_first, int nt0, int ntf, int gi,
+                                               const uint64_t*& f, uint64_t& want) {
+  static_assert(kMaxGroup <= 4, "three boundaries tell four steps apart");
+  const int st = (int)(gi >= nt0) + (int)(gi >= nt0 + ntf) + (int)(gi >= nt0 + 2 * ntf);
+  const int t = t_first + st;
+  f = step_flags(a, t) + (gi - (st == 0 ? 0 : nt0 + (st - 1) * ntf));
+  want = stamp(a.epoch, t);
+}
+
 // claim_next() picks the workgroup's next task (wave 1); it runs alongside the publish.
 template <int D, class ClaimNext>
-__device__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
+__device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
                              ClaimNext&& claim_next) {
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
@@ -702,7 +748,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   step_group = (int)wave_bcast((uint32_t)step_group);
   // The task's ring steps: [t_first, t_end), with the running state in registers
   // from one step to the next.
-  const int t_first = step_group * kGroup, t_end = min(a.n_steps, t_first + kGroup);
+  const int t_first = group_first(a, step_group), t_end = group_end(a, step_group);
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
   const int kvh = p / a.n_hgroups, hgi = p % a.n_hgroups;
   const int h = kvh * a.gqa + hgi * a.hg + (w % a.hg);
@@ -760,37 +806,54 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   f16x8 pb[NP];
 
   // The task's KV phases (PK keys each) form one sequence: the n0 phases of step
-  // t_first, then those of step t_first + 1 (kGroup = 2). The online softmax does not depend on where one
-  // step ends, so one pipeline runs through both steps without draining in between.
-  static_assert(kGroup == 2, "the block sequence covers two steps");
-  auto kend_of = [&](int t) { return (a.causal && t == 0) ? min(a.lk, q_end) : a.lk; };
-  auto n_tiles_of = [&](int t) { return (kend_of(t) + kStageRows - 1) / kStageRows; };
-  const bool two = t_end - t_first > 1;
-  const int n0 = (kend_of(t_first) + PK - 1) / PK;
-  const int nb = n0 + (two ? (kend_of(t_first + 1) + PK - 1) / PK : 0);
+  // t_first, then nfull phases of each later step of the task (up to kMaxGroup steps).
+  // The online softmax does not depend on where one step ends, so one pipeline runs
+  // through every step of the task without draining in between. A block is located by
+  // its step s within the task (scalar compares against the step boundaries) and its
+  // index within that step; tiles likewise count through the task's steps in order
+  // (the task's tile sequence), and `ru` is the frontier below which every tile of that
+  // sequence is known ready.
+  auto kend_of = [&](int t) __attribute__((always_inline)) { return (a.causal && t == 0) ? min(a.lk, q_end) : a.lk; };
+  auto n_tiles_of = [&](int t) __attribute__((always_inline)) { return (kend_of(t) + kStageRows - 1) / kStageRows; };
+  const int nst = t_end - t_first;                   // steps of the task
+  const int nfull = (a.lk + PK - 1) / PK;            // phases of a step after the first
+  const int n0 = (kend_of(t_first) + PK - 1) / PK;   // phases of the first step
+  const int nb = n0 + (nst - 1) * nfull;
+  const int nt0 = n_tiles_of(t_first), ntf = a.n_tiles;
+  const int n_task_tiles = nt0 + (nst - 1) * ntf;
   const int64_t head_off = (int64_t)kvh * a.n_blocks * Block<D>::kBytes + w * 64 * 16;
-  const uint8_t* const sblk_w0 = wave_bcast_ptr(a.slots + (int64_t)(t_first % kSlots) * a.slot_bytes + head_off);
-  const uint8_t* const sblk_w1 =
-      wave_bcast_ptr(a.slots + (int64_t)((t_first + 1) % kSlots) * a.slot_bytes + head_off);
-  auto flags_of = [&](int t) { return a.slot_flags + (t % kSlots) * a.n_tiles; };
+  // This wave's slice of the staged blocks of step st of the task, the ready flags of
+  // step t, and tile gi of the task's tile sequence (per lane) with the stamp it must
+  // hold: plain functions, not lambdas, so no closure is nested three deep (closures
+  // nested that deep kept the compiler from promoting the captured state out of
+  // scratch memory).
+  auto slot_ptr = [&](int st) __attribute__((always_inline)) { return task_slot_ptr<D>(a, t_first + st, head_off); };
 
-  // Flags, in two loads per lane issued together (one round trip): lanes below
-  // min(n_st0, 63) read the ready flags of the staged tiles of step t_first and lane 63
-  // the unit's step t_first-1 stamp (that state must be complete); lanes below
-  // min(n_st1, 64) read those of step t_first+1. Tiles below ru0 (ru1) are then known
-  // ready; later ones are checked when their copy is issued. One acquire covers
-  // everything observed.
-  int ru0, ru1;
+  // Flags, in two loads per lane issued together (one round trip): lanes below 63 read
+  // the ready flags of tiles 0..62 of the task's tile sequence and lane 63 the unit's
+  // step t_first-1 stamp (that state must be complete); every lane reads the flag of
+  // tile 63 + lane. Tiles below the frontier ru are then known ready; later ones are
+  // checked when their copy is issued. One acquire covers everything observed.
+  int ru;
   {
-    const int nt0 = min(n_tiles_of(t_first), 63), nt1 = two ? min(n_tiles_of(t_first + 1), 64) : 0;
     bool r0 = true, r1 = true;
-    if (lane < nt0) r0 = ld64(&flags_of(t_first)[lane]) == stamp(a.epoch, t_first);
-    else if (lane == 63 && t_first > 0) r0 = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t_first - 1);
-    if (lane < nt1) r1 = ld64(&flags_of(t_first + 1)[lane]) == stamp(a.epoch, t_first + 1);
+    const uint64_t* f;
+    uint64_t want;
+    if (lane < 63 && lane < n_task_tiles) {
+      task_tile_flag(a, t_first, nt0, ntf, lane, f, want);
+      r0 = ld64(f) == want;
+    } else if (lane == 63 && t_first > 0) {
+      r0 = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t_first - 1);
+    }
+    if (63 + lane < n_task_tiles) {
+      task_tile_flag(a, t_first, nt0, ntf, 63 + lane, f, want);
+      r1 = ld64(f) == want;
+    }
     const uint64_t nr0 = __ballot(!r0), nr1 = __ballot(!r1);
     const uint64_t tiles_nr0 = nr0 & ~(1ull << 63);
-    ru0 = (int)wave_bcast(tiles_nr0 ? (uint32_t)__builtin_ctzll(tiles_nr0) : (uint32_t)nt0);
-    ru1 = (int)wave_bcast(nr1 ? (uint32_t)__builtin_ctzll(nr1) : (uint32_t)nt1);
+    ru = (int)wave_bcast(tiles_nr0 ? (uint32_t)__builtin_ctzll(tiles_nr0)
+                                   : nr1 ? 63u + (uint32_t)__builtin_ctzll(nr1)
+                                         : (uint32_t)min(n_task_tiles, 127));
     if ((nr0 >> 63) & 1) {
       // The unit's previous step is still running: wait for it (acquires on return).
       ok &= wave_wait_stamp(a, &a.unit_flags[unit], stamp(a.epoch, t_first - 1), waited);
@@ -818,50 +881,71 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     l_run = ml[1];
   }
 
-  // Block vb of the sequence: staged tile known ready, and this wave's slice of it.
-  auto known_ready = [&](int vb) {
-    const bool second = vb >= n0;
-    return vb < nb && ((second ? vb - n0 : vb) * PK) / kStageRows < (second ? ru1 : ru0);
+  // Cursors through the task's block sequence, one for the block the next copy takes
+  // and one for the block the next softmax takes. Each is advanced once per phase by
+  // scalar integer arithmetic: masks come from arithmetic shifts rather than compares,
+  // so no branch and no vector-mask conversion enters the phases. A cursor holds the
+  // block's index within its step (b), the block count of that step (nbs) and the
+  // step (st); the copy cursor also holds the sequence index (k), the tile in the
+  // task's tile sequence and this wave's slice of the block (p).
+  constexpr int kBlocksPerTile = kStageRows / PK;
+  static_assert((kBlocksPerTile & (kBlocksPerTile - 1)) == 0, "blocks per staged tile");
+  int ck = 0, cb = 0, cnbs = n0, cst = 0, ctile = 0;
+  const uint8_t* cptr = slot_ptr(0);
+  auto cur_advance = [&]() __attribute__((always_inline)) {
+    const int nb1 = cb + 1;
+    const int cross = (cnbs - nb1 - 1) >> 31;  // -1 when the step ends here, else 0
+    ck += 1;
+    cb = nb1 & ~cross;
+    cnbs ^= (cnbs ^ nfull) & cross;
+    cst -= cross;
+    ctile += (((cb & (kBlocksPerTile - 1)) - 1) >> 31) & 1;  // a tile starts at its first block
+    cptr = cross ? slot_ptr(cst) : cptr + Phase<D>::kBytes;
   };
-  auto block_w = [&](int vb) {
-    return vb >= n0 ? sblk_w1 + (int64_t)(vb - n0) * Phase<D>::kBytes : sblk_w0 + (int64_t)vb * Phase<D>::kBytes;
+  int sb = 0, snbs = n0, sst = 0;
+  auto sm_advance = [&]() __attribute__((always_inline)) {
+    const int nb1 = sb + 1;
+    const int cross = (snbs - nb1 - 1) >> 31;
+    sb = nb1 & ~cross;
+    snbs ^= (snbs ^ nfull) & cross;
+    sst -= cross;
   };
-  auto issue = [&](int vb, auto stage_tag) {
+  // Copy of the cursor's block into LDS stage S, after making sure its tile is ready.
+  auto issue_cur = [&](auto stage_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_tag)::value;
-    const bool second = vb >= n0;
-    const int j = ((second ? vb - n0 : vb) * PK) / kStageRows;
-    if (j >= (second ? ru1 : ru0)) {
-      // Wait for this tile's flag, then look at all later flags of its step at once
-      // (one load per lane) so the next few tiles need no check.
-      const int t = t_first + (second ? 1 : 0);
-      const uint64_t* flags = flags_of(t);
-      const uint64_t st = stamp(a.epoch, t);
-      const int n_st = n_tiles_of(t);
-      ok &= wave_wait_stamp(a, &flags[j], st, waited);
-      int upto = j + 1;
-      for (int j0 = j + 1; j0 < n_st; j0 += 64) {
-        const bool ready = j0 + lane < n_st && ld64(&flags[j0 + lane]) == st;
-        const uint64_t notready = __ballot(!ready && j0 + lane < n_st);
+    if (ctile >= ru) {
+      // Wait for this tile's flag, then look at the later flags of the task's tile
+      // sequence 64 at a time (one load per lane) so the next tiles need no check.
+      const int t = t_first + cst;
+      ok &= wave_wait_stamp(a, step_flags(a, t) + cb / kBlocksPerTile, stamp(a.epoch, t), waited);
+      int upto = ctile + 1;
+      for (int g0 = ctile + 1; g0 < n_task_tiles; g0 += 64) {
+        bool ready = false;
+        if (g0 + lane < n_task_tiles) {
+          const uint64_t* f;
+          uint64_t want;
+          task_tile_flag(a, t_first, nt0, ntf, g0 + lane, f, want);
+          ready = ld64(f) == want;
+        }
+        const uint64_t notready = __ballot(!ready && g0 + lane < n_task_tiles);
         if (notready) {
-          upto = j0 + (int)__builtin_ctzll(notready);
+          upto = g0 + (int)__builtin_ctzll(notready);
           break;
         }
-        upto = min(n_st, j0 + 64);
+        upto = min(n_task_tiles, g0 + 64);
       }
-      if (upto > j + 1) fence_acquire();
-      upto = (int)wave_bcast((uint32_t)upto);
-      if (second) ru1 = upto;
-      else ru0 = upto;
+      if (upto > ctile + 1) fence_acquire();
+      ru = (int)wave_bcast((uint32_t)upto);
     }
-    dma_block<D, S>(block_w(vb), cl, m0w_task);
+    dma_block<D, S>(cptr, cl, m0w_task);
   };
 
-  // Online-softmax update for block vb (FlashAttention-2), producing fp16 Pᵀ.
-  auto softmax = [&](int vb) {
+  // Online-softmax update for the softmax cursor's block (FlashAttention-2), producing
+  // fp16 Pᵀ.
+  auto softmax = [&]() __attribute__((always_inline)) {
     // Masks: ragged key tail, and keys after the query on the diagonal step.
-    const bool second = vb >= n0;
-    const bool diag = a.causal && t_first == 0 && !second;
-    const int k0 = (second ? vb - n0 : vb) * PK;
+    const bool diag = a.causal && t_first == 0 && sst == 0;
+    const int k0 = sb * PK;
     if (k0 + PK > a.lk || (diag && k0 + PK - 1 > q0w)) {
       // Element i of s[kb] holds key k0 + kb*32 + (i/4)*8 + hi*4 + i%4; it is visible iff
       // that key is below lim + k0 + hi*4 (lim is per lane, the offsets constants).
@@ -889,7 +973,7 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
     // as any sum above kSumMax does. (A v_dot2c sum would not co-issue with the other
     // wave's MFMAs.)
     float lsum;
-    auto exp_block = [&](float mref) {
+    auto exp_block = [&](float mref) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
@@ -948,15 +1032,15 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   // undo the ping-pong. Empty volatile asm statements, which keep their order with
   // the barriers, pin each phase's inputs after its barrier and its outputs before
   // the next one.
-  auto pin_scores = [&]() {
+  auto pin_scores = [&]() __attribute__((always_inline)) {
     if constexpr (NS == 2) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     else asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
   };
-  auto pin_acc = [&]() {
+  auto pin_acc = [&]() __attribute__((always_inline)) {
     if constexpr (DB == 4) asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
     else asm volatile("" : "+v"(o[0]), "+v"(o[1]));
   };
-  auto pin_state = [&]() {
+  auto pin_state = [&]() __attribute__((always_inline)) {
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(m_run), "+v"(l_run));
     if constexpr (NP == 8) asm volatile("" : "+v"(pb[4]), "+v"(pb[5]), "+v"(pb[6]), "+v"(pb[7]));
     pin_acc();
@@ -970,55 +1054,72 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   // at least one block copy issued after the one it needs, and waiting until at most
   // NI copy instructions are outstanding is enough (it may also cover a discarded
   // copy).
-  auto wait_block = [&]() { wait_vm(NI); };
-  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4.
-  auto mstep = [&](int m, auto stage_tag, auto mfmas) {
+  auto wait_block = [&]() __attribute__((always_inline)) { wait_vm(NI); };
+  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4. Returns whether the
+  // cursor's block still has to be copied (its tile was not known ready), which the
+  // caller then does with issue_cur before advancing the cursor: kept out of this
+  // lambda, because with it inside, the closures nested here kept the compiler from
+  // promoting the captured state out of scratch memory.
+  auto mstep = [&](int m, auto stage_tag, auto mfmas) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_tag)::value;
     if (m < nb) wait_block();
     __builtin_amdgcn_s_barrier();
-    const int kn = m + 2;
-    const bool ready = known_ready(kn);  // from scalars only: stays in SALU
+    // The copy cursor is at block m + 2.
+    const bool exists = ck < nb;
+    const bool ready = exists && ctile < ru;  // from scalars only: stays in SALU
     // Base of this wave's LDS slice, opaque per phase so the compiler adds the stage
     // and instruction offsets here (scalar adds) instead of keeping sixteen of them
     // in SGPRs across the loop.
-    uint32_t m0w = m0w_task;
+    uint32_t m0w = wave_bcast(m0w_task);
     asm volatile("" : "+s"(m0w));
-    mfmas(ready ? block_w(kn) : discard_w, m0w);
+    mfmas(wave_bcast_ptr(ready ? cptr : discard_w), m0w);
     pin_scores();
     pin_acc();
-    if (kn < nb && !ready) issue(kn, std::integral_constant<int, (S + 2) % kStages>{});
+    return exists && !ready;
   };
   // Operand registers of the next matrix phase's first LDS reads, issued at the end of
   // each softmax phase (MPhase::prefetch).
   u32x4 pre[MPhase<D, 0, true, true>::R];
   // V(m), then the first operand reads of M(m+1), whose stage is SN.
-  auto vstep = [&](int m, auto next_stage_tag) {
+  auto vstep = [&](int m, auto next_stage_tag) __attribute__((always_inline)) {
     constexpr int SN = decltype(next_stage_tag)::value;
     if (m + 1 < nb) wait_block();
     __builtin_amdgcn_s_barrier();
     pin_scores();
-    softmax(m);
+    softmax();
+    sm_advance();
     pin_state();
     MPhase<D, SN, true, true>::prefetch(pre, la);
   };
 #define MKRA_PVQK(S) \
-  [&](const uint8_t* src, uint32_t m0w) { MPhase<D, S, true, true>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); }
+  [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) { MPhase<D, S, true, true>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); }
 #define MKRA_PV(S) \
-  [&](const uint8_t* src, uint32_t m0w) { \
+  [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) { \
     MPhase<D, S, true, false, false>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); \
   }
   // nb >= 1: every unit has keys (Lk >= 1, and the diagonal step covers at least the
   // unit's first query).
-  issue(0, std::integral_constant<int, 0>{});
-  if (1 < nb) issue(1, std::integral_constant<int, 1>{});
+  issue_cur(std::integral_constant<int, 0>{});
+  cur_advance();
+  if (1 < nb) issue_cur(std::integral_constant<int, 1>{});
   else dma_block<D, 1>(discard_w, cl, m0w_task);  // discarded (see the copy rule above)
+  cur_advance();
   if (grp) {
     wait_block();
     __builtin_amdgcn_s_barrier();
   }
-  mstep(0, std::integral_constant<int, 0>{}, [&](const uint8_t* src, uint32_t m0w) {
+  // M(m) in stage S, then the copy of the cursor's block if its tile was not known
+  // ready, into the stage M(m) left for it, and the cursor's advance.
+#define MKRA_M(m, S, MFMAS)                                                         \
+  do {                                                                              \
+    if (mstep(m, std::integral_constant<int, S>{}, MFMAS))                          \
+      issue_cur(std::integral_constant<int, ((S) + 2) % kStages>{});                \
+    cur_advance();                                                                  \
+  } while (0)
+  auto first_qk = [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) {
     MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
-  });
+  };
+  MKRA_M(0, 0, first_qk);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
@@ -1026,35 +1127,37 @@ __device__ void compute_task(const KernelArgs& a, int unit, int step_group, int 
   vstep(0, S1{});
   int m = 1;
   for (; m + 3 < nb; m += kStages) {
-    mstep(m, S1{}, MKRA_PVQK(1));
+    MKRA_M(m, 1, MKRA_PVQK(1));
     vstep(m, S2{});
-    mstep(m + 1, S2{}, MKRA_PVQK(2));
+    MKRA_M(m + 1, 2, MKRA_PVQK(2));
     vstep(m + 1, S3{});
-    mstep(m + 2, S3{}, MKRA_PVQK(3));
+    MKRA_M(m + 2, 3, MKRA_PVQK(3));
     vstep(m + 2, S0{});
-    mstep(m + 3, S0{}, MKRA_PVQK(0));
+    MKRA_M(m + 3, 0, MKRA_PVQK(0));
     vstep(m + 3, S1{});
   }
   if (m < nb) {
-    mstep(m, S1{}, MKRA_PVQK(1));
+    MKRA_M(m, 1, MKRA_PVQK(1));
     vstep(m, S2{});
     if (++m < nb) {
-      mstep(m, S2{}, MKRA_PVQK(2));
+      MKRA_M(m, 2, MKRA_PVQK(2));
       vstep(m, S3{});
       if (++m < nb) {
-        mstep(m, S3{}, MKRA_PVQK(3));
+        MKRA_M(m, 3, MKRA_PVQK(3));
         vstep(m, S0{});
         ++m;
       }
     }
   }
-  // M(nb): PV of the last block only; no wait follows, so it copies nothing.
+  // M(nb): PV of the last block only; no wait follows, so it copies nothing (the
+  // cursor is past the sequence, so mstep asks for no copy either).
   switch (nb & 3) {
-    case 0: mstep(nb, std::integral_constant<int, 0>{}, MKRA_PV(0)); break;
-    case 1: mstep(nb, std::integral_constant<int, 1>{}, MKRA_PV(1)); break;
-    case 2: mstep(nb, std::integral_constant<int, 2>{}, MKRA_PV(2)); break;
-    default: mstep(nb, std::integral_constant<int, 3>{}, MKRA_PV(3)); break;
+    case 0: mstep(nb, S0{}, MKRA_PV(0)); break;
+    case 1: mstep(nb, S1{}, MKRA_PV(1)); break;
+    case 2: mstep(nb, S2{}, MKRA_PV(2)); break;
+    default: mstep(nb, S3{}, MKRA_PV(3)); break;
   }
+#undef MKRA_M
 #undef MKRA_PVQK
 #undef MKRA_PV
   if (!grp) __builtin_amdgcn_s_barrier();
@@ -1136,13 +1239,14 @@ struct Sched {
 // round trip plus, for a compute task, one compare-and-swap (these words are shared
 // by all XCDs, so each access goes to memory).
 //
-// Compute tasks: a task is one unit for kGroup consecutive ring steps (a step group).
+// Compute tasks: a task is one unit for the consecutive ring steps of a step group.
 // Each XCD has a queue of the units of its head groups, group-major, so units that
 // read the same KV head share an L2. A workgroup takes from its own queue only while
 // that queue is at most one group ahead of the slowest queue, else from the slowest
 // queue. A task of group g needs its unit's group g-1 (claimed earlier, same queue
-// order) and staging of its steps, whose slots are released once group g - kSlots/kGroup
-// is complete (at most g-2, as kSlots >= 2 kGroup); every task of group g-2 is claimed
+// order) and staging of its steps, whose slots are released once every unit is past
+// step group_end(g) - 1 - kSlots, which lies in group g-2 or earlier since no group has
+// more than kSlots/2 steps; every task of group g-2 is claimed
 // when the rule admits group
 // g, so the schedule cannot deadlock whatever subset of workgroups is resident. Within
 // a group a queue runs its units from the last, so on the causal diagonal step the
@@ -1264,7 +1368,7 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     uint32_t h = sh;
     bool assist = false;
     int released_below = 0;  // steps whose slot is known released
-    const int pend_last = min(a.n_steps, (st->pend_g + 1) * kGroup) - 1;  // last step the task runs
+    const int pend_last = group_end(a, st->pend_g) - 1;  // last step the task runs
     for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
       const int step = (int)h / a.n_tiles;
       if (step > pend_last) break;
@@ -1347,7 +1451,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
       claimed = true;
       if (tid == 0) {
         const uint64_t busy = ticks() - t0 - w0;
-        const int t_first = y * kGroup, t_end = min(a.n_steps, t_first + kGroup);
+        const int t_first = group_first(a, y), t_end = group_end(a, y);
         add64(&a.ctrl->compute_ticks.v, busy);
         add32(&a.ctrl->compute_done.v, (uint32_t)(t_end - t_first));  // unit-steps
         add64(&a.ctrl->compute_wait_ticks.v, w0);

@@ -54,7 +54,7 @@ def test_probe_library_exports_its_two_entry_points():
 
 
 def test_abi_version():
-    assert mk.mk_abi_version() == 1
+    assert mk.mk_abi_version() == 2
 
 
 def test_struct_layouts_match_the_header():

@@ -135,6 +135,14 @@ SPLIT_VARIANTS = [
     dict(grid_wgs=2),
     dict(grid_wgs=8),
     dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, debug_flags=1),
+    dict(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER),
+    dict(steps_per_task=1),
+    dict(steps_per_task=2),
+    dict(steps_per_task=3),
+    dict(steps_per_task=3, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, stage_delay_ticks=3000),
+    dict(steps_per_task=4, grid_wgs=3),
+    dict(steps_per_task=4, tail_steps=3, tail_steps_per_task=1),
+    dict(steps_per_task=3, tail_steps=4, tail_steps_per_task=2, grid_wgs=5),
 ]
 
 
@@ -285,11 +293,34 @@ def test_wait_bound_reports_timeout_and_recovers():
     check_full(cfg, seed=41)
 
 
-def test_stats_and_controller_follow_eq2():
+def group_firsts(n_steps, g, tail_steps, tail_g):
+    """First step of every step group, per the rule the header documents: groups of g
+    steps, the last tail_steps steps in groups of tail_g."""
+    n_big = max(0, n_steps - tail_steps) // g
+    firsts = [i * g for i in range(n_big)]
+    t = n_big * g
+    while t < n_steps:
+        firsts.append(t)
+        t += tail_g
+    return firsts
+
+
+@pytest.mark.parametrize("mode,groups", [("adaptive", (4, 0, 2)), ("paper", (4, 0, 2)), ("adaptive", (2, -1, 1)),
+                                         ("adaptive", (3, 2, 1))],
+                         ids=["adaptive-g4", "paper-g4", "adaptive-g2", "adaptive-g3-tail2x1"])
+def test_stats_and_controller_follow_eq2(mode, groups):
+    """Every controller update of a traced run sets the target Eq. (2) gives for the
+    inputs it records. ADAPTIVE: R_p leaves out the last step group's unit-steps.
+    ADAPTIVE_PAPER: R_p is every unclaimed unit-step, and C_p, C_s are plain measured
+    averages; the first update's R_p then equals the whole compute work minus what
+    was claimed before it."""
     cfg = CONFIGS[1]
     q, kv = make_inputs(cfg, seed=1)
-    announce("traced adaptive run")
-    out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2)
+    announce(f"traced {mode} run")
+    split = mk.MK_SPLIT_ADAPTIVE if mode == "adaptive" else mk.MK_SPLIT_ADAPTIVE_PAPER
+    g, tail_steps, tail_g = groups
+    out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2,
+                           split_mode=split, steps_per_task=g, tail_steps=tail_steps, tail_steps_per_task=tail_g)
     print("    stats:", st, flush=True)
     assert st["status"] == 0
     assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]
@@ -300,10 +331,13 @@ def test_stats_and_controller_follow_eq2():
     stage = [r for r in recs if r[2] == 2]
     assert len(comp) == st["compute_tasks_done"] and len(stage) == st["staging_tasks_done"]
     assert len(ctrl) == st["controller_updates"] and len(ctrl) >= 1
-    # R_p as Eq. (2) takes it: unclaimed unit-steps outside the last step group (those
-    # follow the last staging task whatever the split).
-    n_groups = (st["n_steps"] + 1) // 2
-    rp_max = st["n_units"] * 2 * (n_groups - 1)
+    # R_p as Eq. (2) takes it: unclaimed unit-steps, outside the last step group in
+    # ADAPTIVE mode (those follow the last staging task whatever the split).
+    # This workload's units fit the grid, so the default tail is none; explicit tails
+    # follow the documented rule.
+    firsts = group_firsts(st["n_steps"], g, max(tail_steps, 0), tail_g)
+    assert st["steps_per_task"] == g and st["step_groups"] == len(firsts), (st, firsts)
+    rp_max = st["n_units"] * (firsts[-1] if mode == "adaptive" else st["n_steps"])
     for r in ctrl:
         rp, rs, cp, cs, b, target = r[3:9]
         assert 0 <= rp <= rp_max, (r, rp_max)
