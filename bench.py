@@ -1,7 +1,8 @@
 """Benchmark of the per-rank ring-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep] [--size-sweep] [--verify] [--copy-calibration-mib M]
+                    [--no-cpu-baseline] [--sweep] [--size-sweep] [--unfused] [--verify]
+                    [--copy-calibration-mib M]
     python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
     python bench.py --probes    (MFMA-stream and vector-ALU probes; prints a table)
 
@@ -88,36 +89,88 @@ def _counter_rows(run_dir):
     return rows
 
 
+def _per_dispatch(rows, counter, kernel_sub):
+    """Values of `counter` for the dispatches whose kernel name contains kernel_sub,
+    in dispatch order."""
+    sel = [r for r in rows if r["Counter_Name"] == counter and kernel_sub in r["Kernel_Name"]]
+    sel.sort(key=lambda r: int(r.get("Dispatch_Id", 0) or 0))
+    return [float(r["Counter_Value"]) for r in sel]
+
+
+def _copy_dispatch(rows, counter):
+    """Mean value of `counter` over the largest plain device copies (rocclr copyBuffer
+    dispatches of the largest grid): the known-size reference."""
+    copies = [r for r in rows if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    if not copies:
+        return None
+    gmax = max(int(r["Grid_Size"]) for r in copies)
+    cal = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == gmax]
+    return sum(cal) / len(cal)
+
+
 def write_traffic(cfg, pmc_dir, copy_mib):
-    """HBM bytes per launch of the ring kernel from two rocprofv3 --pmc runs of
-    `bench.py --copy-calibration-mib M` (FETCH_SIZE under pmc_dir/fetch, WRITE_SIZE
-    under pmc_dir/write). Each counter is scaled by what it reads for the plain
-    device copy of M MiB in the same run (largest copyBuffer dispatches)."""
-    res = {}
-    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
-        rows = [r for r in _counter_rows(os.path.join(pmc_dir, sub)) if r["Counter_Name"] == counter]
-        ring = [float(r["Counter_Value"]) for r in rows if "ring_attn_kernel" in r["Kernel_Name"]]
-        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        if not ring or not copies:
-            raise SystemExit(f"{counter}: missing ring kernel or copy dispatches in {pmc_dir}/{sub}")
-        gmax = max(int(r["Grid_Size"]) for r in copies)
-        cal = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == gmax]
-        copy_kib = sum(cal) / len(cal)
-        moved = copy_mib * 1024.0  # KiB read (FETCH) or written (WRITE) by the copy
-        scale = moved / copy_kib
-        kib = sum(ring) / len(ring)
-        res[counter] = {"kib_per_dispatch": kib, "dispatches": len(ring), "copy_kib_per_dispatch": copy_kib,
-                        "copy_dispatches": len(cal), "scale": scale, "bytes_per_launch": kib * 1024.0 * scale}
-    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    """HBM bytes per launch of the ring kernel from rocprofv3 --pmc runs of
+    `bench.py --copy-calibration-mib M`, one counter set per sub-directory of pmc_dir:
+      dram/  TCC_EA0_RDREQ_DRAM_32B_sum, TCC_EA0_WRREQ_WRITE_DRAM_32B_sum: L2-to-memory
+             reads and writes in 32-byte units (a 64-byte request counts 2, a 128-byte
+             one 4), so bytes = 32 x count with no calibration;
+      fetch/ FETCH_SIZE and write/ WRITE_SIZE (KiB by rocprofv3's derived formulas),
+             each scaled by what it reads for the plain copy of M MiB in the same run;
+      req/   TCC_BUBBLE_sum, TCC_EA0_RDREQ_128B_sum, TCC_EA0_RDREQ_sum,
+             TCC_EA0_RDREQ_32B_sum: the request-size mix FETCH_SIZE's formula is built
+             from (reported for the copy and the ring kernel).
+    The ring kernel's value per launch is the median over its dispatches after the
+    first. The 32-byte counters give hbm_bytes_per_launch when present."""
+    import statistics as st
+
+    res = {"copy_calibration_mib": copy_mib}
+    moved = copy_mib * 1024.0 * 1024.0
+
+    def med(v):
+        return st.median(v[1:] if len(v) > 1 else v)
+
+    sub = os.path.join(pmc_dir, "dram")
+    if os.path.isdir(sub):
+        rows = _counter_rows(sub)
+        d = {}
+        for counter, key in (("TCC_EA0_RDREQ_DRAM_32B_sum", "read"), ("TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "write")):
+            ring = _per_dispatch(rows, counter, "ring_attn_kernel")
+            cp = _copy_dispatch(rows, counter)
+            d[key] = {"counter": counter, "ring_bytes_per_launch": 32.0 * med(ring), "dispatches": len(ring),
+                      "copy_bytes": 32.0 * cp if cp is not None else None,
+                      "copy_over_moved": round(32.0 * cp / moved, 4) if cp is not None else None}
+        res["dram_32b"] = d
+    for name, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        sub = os.path.join(pmc_dir, name)
+        if not os.path.isdir(sub):
+            continue
+        rows = _counter_rows(sub)
+        ring = _per_dispatch(rows, counter, "ring_attn_kernel")
+        cp = _copy_dispatch(rows, counter)
+        scale = (copy_mib * 1024.0) / cp
+        res[counter] = {"ring_kib_per_dispatch": med(ring), "dispatches": len(ring), "copy_kib_per_dispatch": cp,
+                        "scale": scale, "bytes_per_launch": med(ring) * 1024.0 * scale}
+    sub = os.path.join(pmc_dir, "req")
+    if os.path.isdir(sub):
+        rows = _counter_rows(sub)
+        mix = {}
+        for counter in ("TCC_BUBBLE_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum"):
+            ring = _per_dispatch(rows, counter, "ring_attn_kernel")
+            mix[counter] = {"ring_per_launch": med(ring) if ring else None, "copy": _copy_dispatch(rows, counter)}
+        res["read_request_mix"] = mix
+    if "dram_32b" in res:
+        total = res["dram_32b"]["read"]["ring_bytes_per_launch"] + res["dram_32b"]["write"]["ring_bytes_per_launch"]
+        res["source"] = "TCC_EA0_RDREQ_DRAM_32B_sum + TCC_EA0_WRREQ_WRITE_DRAM_32B_sum, x 32 bytes"
+    else:
+        total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+        res["source"] = "FETCH_SIZE + WRITE_SIZE, copy-calibrated"
     out = {"workload": cfg.name, "kernel": "mkra::ring_attn_kernel<%d>" % cfg.d, "kernel_sha": kernel_hash(),
-           "copy_calibration_mib": copy_mib, "counters": res, "hbm_bytes_per_launch": int(total),
-           "algorithmic_bytes": algorithmic_bytes(cfg)}
+           "counters": res, "hbm_bytes_per_launch": int(total), "algorithmic_bytes": algorithmic_bytes(cfg)}
     path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    log(f"[bench] wrote {path}: {total / 1e6:.1f} MB per launch "
-        f"(FETCH x{res['FETCH_SIZE']['scale']:.3f}, WRITE x{res['WRITE_SIZE']['scale']:.3f})")
+    log(f"[bench] wrote {path}: {total / 1e6:.1f} MB per launch ({res['source']})")
 
 
 def staging_summary(cfg, stats, ms):
@@ -150,9 +203,11 @@ def split_sweep(mk, timed, k):
     for n in SPLITS:
         res[f"fixed{n}"] = timed(k, mk.default_opts(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n))[0]
     res["adaptive"] = timed(k)[0]
-    best_name = min((n for n in res if n != "adaptive"), key=lambda n: res[n])
+    res["adaptive_paper"] = timed(k, mk.default_opts(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER))[0]
+    best_name = min((n for n in res if not n.startswith("adaptive")), key=lambda n: res[n])
     return {"ms": {n: round(v, 4) for n, v in res.items()}, "best_fixed": best_name,
-            "best_fixed_ms": round(res[best_name], 4), "adaptive_over_best": round(res["adaptive"] / res[best_name], 3)}
+            "best_fixed_ms": round(res[best_name], 4), "adaptive_over_best": round(res["adaptive"] / res[best_name], 3),
+            "adaptive_paper_over_best": round(res["adaptive_paper"] / res[best_name], 3)}
 
 
 def run_size_sweep(torch, mk, make_inputs, stream):
@@ -161,7 +216,7 @@ def run_size_sweep(torch, mk, make_inputs, stream):
     from ring_inputs import RingConfig
 
     out = []
-    for total in (6144, 12288, 24576, 49152, 98304, 196608):
+    for total in SWEEP_SIZES:
         L = total // 16
         cfg = RingConfig(f"seq{total // 1024}k_r15of16_L{L}_h32kv8_d128_causal", rank=15, n_chunks=16, lq=L, lk=L,
                          hq=32, hkv=8, d=128, causal=True)
@@ -193,10 +248,76 @@ def run_size_sweep(torch, mk, make_inputs, stream):
         sw["chunk_rows"] = L
         out.append(sw)
         log(f"[bench] size {total}: adaptive {sw['ms']['adaptive']:.3f} ms ({sw['tflops_adaptive']} TFLOP/s), "
-            f"best fixed {sw['best_fixed']} {sw['best_fixed_ms']:.3f} ms, adaptive/best {sw['adaptive_over_best']}")
+            f"best fixed {sw['best_fixed']} {sw['best_fixed_ms']:.3f} ms, adaptive/best {sw['adaptive_over_best']}, "
+            f"paper Eq. (2)/best {sw['adaptive_paper_over_best']}")
         del qg, kvg, o, l
         torch.cuda.empty_cache()
     return out
+
+
+SWEEP_SIZES = (6144, 12288, 24576, 49152, 98304, 196608)
+COPY_WGS = (4, 8, 16, 32)
+
+
+def run_unfused_sweep(torch, mk, make_inputs, stream, sizes=SWEEP_SIZES):
+    """The fused kernel against the unfused two-stream baseline (per-step staging and
+    compute launches, chunks released at kernel boundaries: Figure 1(b) of the paper)
+    over total sequence sizes 6K..192K: rank 15 of a 16-rank causal GQA ring, Hq = 32,
+    Hkv = 8, D = 128. The unfused leg takes the best of COPY_WGS staging workgroups.
+    Returns rows and logs a markdown table."""
+    from ring_inputs import RingConfig
+
+    copy = torch.cuda.Stream()
+    rows = []
+    for total in sizes:
+        L = total // 16
+        cfg = RingConfig(f"seq{total // 1024}k_r15of16_L{L}_h32kv8_d128_causal", rank=15, n_chunks=16, lq=L, lk=L,
+                         hq=32, hkv=8, d=128, causal=True)
+        q, kv = make_inputs(cfg, seed=7)
+        qg, kvg = q.cuda(), kv.cuda()
+        del q, kv
+        o = torch.empty_like(qg)
+        lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device="cuda")
+
+        def timed_call(fn, k):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(k):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / k
+
+        k = max(3, min(50, int(60 / max(1.0, (L / 4096) ** 2 * 4.2))))
+        args = (qg, kvg, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, o, lse)
+        fused = timed_call(lambda: mk.mk_ring_attn_fwd(*args, stream=stream), k)
+        paper = timed_call(lambda: mk.mk_ring_attn_fwd_ex(
+            *args, stream=stream, opts=mk.default_opts(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)), k)
+        unf = {n: timed_call(lambda: mk.mk_ring_attn_fwd_unfused(*args, copy, n, stream=stream), k) for n in COPY_WGS}
+        mk.mk_ring_attn_status(stream)
+        best = min(unf, key=unf.get)
+        flops = algorithmic_flops(cfg)
+        rows.append({"total_seq": total, "chunk_rows": L, "fused_ms": round(fused, 4),
+                     "fused_paper_eq2_ms": round(paper, 4),
+                     "unfused_ms": {str(n): round(v, 4) for n, v in unf.items()}, "unfused_best_copy_wgs": best,
+                     "unfused_best_ms": round(unf[best], 4), "unfused_over_fused": round(unf[best] / fused, 3),
+                     "fused_tflops": round(flops / (fused * 1e-3) / 1e12, 1),
+                     "unfused_tflops": round(flops / (unf[best] * 1e-3) / 1e12, 1)})
+        log(f"[bench] unfused size {total}: fused {fused:.3f} ms, paper Eq. (2) {paper:.3f} ms, unfused best "
+            f"{unf[best]:.3f} ms ({best} copy WGs), unfused/fused {unf[best] / fused:.3f}")
+        del qg, kvg, o, lse
+        torch.cuda.empty_cache()
+    table = ["| total tokens | chunk rows | fused ms | fused, paper Eq. (2) ms | unfused best ms (copy WGs) | "
+             "unfused / fused | fused TFLOP/s | unfused TFLOP/s |", "|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        table.append(f"| {r['total_seq']} | {r['chunk_rows']} | {r['fused_ms']:.3f} | {r['fused_paper_eq2_ms']:.3f} | "
+                     f"{r['unfused_best_ms']:.3f} ({r['unfused_best_copy_wgs']}) | {r['unfused_over_fused']:.3f} | "
+                     f"{r['fused_tflops']} | {r['unfused_tflops']} |")
+    log("\n".join(table))
+    return rows
 
 
 PROBE_MODES = (
@@ -357,6 +478,9 @@ def main():
                     help="also time fixed staging splits {1..64} against the adaptive split (Fig. 3's metric)")
     ap.add_argument("--size-sweep", action="store_true",
                     help="also run the split sweep over total sequence sizes 6K..192K (16 ranks, rank 15)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="also time the unfused two-stream baseline against the fused kernel over sequence sizes "
+                         "6K..192K (16 ranks, rank 15)")
     ap.add_argument("--verify", action="store_true", help="check sampled rows against the oracle (stderr)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), the known-size "
@@ -477,6 +601,9 @@ def main():
     size_sweep = None
     if args.size_sweep:
         size_sweep = run_size_sweep(torch, mk, make_inputs, stream)
+    unfused_sweep = None
+    if args.unfused:
+        unfused_sweep = run_unfused_sweep(torch, mk, make_inputs, stream)
 
     traffic = stored_traffic(cfg.name)
     # Average shader clock over every workgroup's lifetime (s_memtime cycles against
@@ -529,6 +656,8 @@ def main():
         line["split_sweep"] = sweep
     if size_sweep is not None:
         line["size_sweep"] = size_sweep
+    if unfused_sweep is not None:
+        line["unfused_sweep"] = unfused_sweep
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
         line["cpu_baseline"] = cpu_baseline(cfg, q, kv, args.cpu_rows)

@@ -73,7 +73,7 @@ typedef struct {
                                   §3.2 re-targets the staging-workgroup count with
                                   Eq. (2) from measured per-task costs, with two
                                   changes to its inputs: R_p leaves out the compute
-                                  of the last step group (it can only follow the last
+                                  of the last ring step (it can only follow the last
                                   staging task), and C_p, C_s are averaged with the
                                   cost model's priors weighted as one ring step (C_s
                                   counting a staging task's waits for a free slot).
@@ -160,7 +160,7 @@ typedef struct {
  * v3 wait ticks), 2 staging task (v0 task, v1 step, v2 tile, v3 start tick, v4 1 if
  * done by a stalled compute workgroup, v5 element offset of its destination in the
  * slot ring, -1 if it did not copy), 3 controller update (v0 R_p as Eq. (2) takes it:
- * unclaimed compute unit-steps, outside the last step group in ADAPTIVE mode, v1 R_s, v2 C_p,
+ * unclaimed compute unit-steps, less the last ring step's in ADAPTIVE mode, v1 R_s, v2 C_p,
  * v3 C_s, v4 blocks B, v5 new target), 4 role switch (v0 new role: 0 compute,
  * 1 staging, v1 staging-role count after it). t: tick at which it was written. */
 typedef struct {
@@ -235,6 +235,30 @@ mk_status mk_ring_attn_fwd_noalloc(const mk_tensor* q, const mk_tensor* kv_chunk
                                    int causal, int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream);
 
 #define MKRA_NOALLOC_SCRATCH_BYTES (256ull << 20)
+
+/* The unfused two-stream baseline the fused kernel is measured against (mKernel paper
+ * §1, Figure 1(b): a two-stream pipeline that releases each chunk only at a kernel
+ * boundary; §5.4 compares the fused Ring Attention with attention kernels followed by
+ * a separate collective). A measurement leg, not a second way to compute: same
+ * arguments and results as mk_ring_attn_fwd (bitwise equal to mk_ring_attn_fwd_ex with
+ * steps_per_task = 1 and tail_steps = -1), computed by the same kernel's device code
+ * launched once per ring step:
+ *  - copy_stream: for each step t, a staging-only launch with copy_wgs workgroups
+ *    copies step t's chunk into slot t mod 8 of the workspace's slot ring, after
+ *    waiting (stream event) for the compute launch of step t-8, the last reader of
+ *    that slot;
+ *  - stream: for each step t, after waiting for that staging launch, a compute-only
+ *    launch runs every unit's step t on the rest of the workgroups, carrying the
+ *    running state through the workspace from step to step.
+ * copy_stream must be a different stream of the same device than `stream`; the call
+ * makes copy_stream wait for the work already on `stream`, and the last compute
+ * launch on `stream` follows every staging launch, so later work on `stream` sees the
+ * whole call done. copy_wgs >= 1 (clamped to leave at least one compute workgroup).
+ * The workspace is the one of `stream`; device-side errors of either stream's
+ * launches are reported by mk_ring_attn_status(stream). */
+mk_status mk_ring_attn_fwd_unfused(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank, int causal,
+                                   int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream,
+                                   hipStream_t copy_stream, int copy_wgs);
 
 /* Fills *opts with the defaults (adaptive split, all CUs, 10 s wait bound). */
 void mk_ring_attn_default_opts(mk_ring_attn_opts* opts);

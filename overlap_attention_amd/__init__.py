@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     mk_ring_attn_fwd,
     mk_ring_attn_fwd_ex,
     mk_ring_attn_fwd_noalloc,
+    mk_ring_attn_fwd_unfused,
     mk_ring_attn_status,
     mk_ring_attn_trace,
     ring_attn_fwd,

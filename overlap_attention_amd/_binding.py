@@ -99,6 +99,10 @@ _PROTOTYPES = {
     "mk_ring_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(mk_tensor), ctypes.POINTER(mk_tensor), ctypes.c_int,
                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(mk_tensor),
                                                 ctypes.POINTER(mk_tensor), ctypes.c_void_p]),
+    "mk_ring_attn_fwd_unfused": (ctypes.c_int, [ctypes.POINTER(mk_tensor), ctypes.POINTER(mk_tensor), ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(mk_tensor),
+                                                ctypes.POINTER(mk_tensor), ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int]),
     "mk_ring_attn_default_opts": (None, [ctypes.POINTER(mk_ring_attn_opts)]),
     "mk_ring_attn_status": (ctypes.c_int, [ctypes.c_void_p]),
     "mk_ring_attn_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(mk_trace_record), ctypes.c_int64,
@@ -202,6 +206,17 @@ def mk_ring_attn_fwd_noalloc(q, kv_chunks, n_chunks: int, rank: int, causal: boo
     qd, kd, od, ld = tensor_desc(q), tensor_desc(kv_chunks), tensor_desc(out), tensor_desc(lse)
     _check(lib.mk_ring_attn_fwd_noalloc(ctypes.byref(qd), ctypes.byref(kd), n_chunks, rank, int(bool(causal)),
                                         gqa_ratio, ctypes.byref(od), ctypes.byref(ld), _stream_ptr(stream)))
+
+
+def mk_ring_attn_fwd_unfused(q, kv_chunks, n_chunks: int, rank: int, causal: bool, gqa_ratio: int, out, lse,
+                             copy_stream, copy_wgs: int, stream=None) -> None:
+    """Thin call of mk_ring_attn_fwd_unfused (the two-stream unfused baseline); copy_stream
+    is a torch stream other than `stream`."""
+    lib = load_library()
+    qd, kd, od, ld = tensor_desc(q), tensor_desc(kv_chunks), tensor_desc(out), tensor_desc(lse)
+    _check(lib.mk_ring_attn_fwd_unfused(ctypes.byref(qd), ctypes.byref(kd), n_chunks, rank, int(bool(causal)),
+                                        gqa_ratio, ctypes.byref(od), ctypes.byref(ld), _stream_ptr(stream),
+                                        _stream_ptr(copy_stream), copy_wgs))
 
 
 def mk_ring_attn_status(stream=None) -> int:

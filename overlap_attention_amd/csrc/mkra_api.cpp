@@ -61,6 +61,11 @@ struct Workspace {
   TraceRec* trace = nullptr;
   int trace_cap = 0;
   bool traced_last = false;
+  // The unfused baseline: the control block and status of its staging launches (which
+  // run beside its compute launches), and one event per step and stream.
+  DevCtrl* ctrl_copy = nullptr;
+  DevStatus* status_copy = nullptr;
+  std::vector<hipEvent_t> ev_staged, ev_computed;
 };
 
 std::mutex g_mu;
@@ -113,6 +118,10 @@ void free_ws(Workspace* w) {
     hipFree(w->slots);
     hipFree(w->acc);
     hipFree(w->trace);
+    hipFree(w->ctrl_copy);
+    hipFree(w->status_copy);
+    for (hipEvent_t ev : w->ev_staged) hipEventDestroy(ev);
+    for (hipEvent_t ev : w->ev_computed) hipEventDestroy(ev);
     hipSetDevice(cur);
   }
   delete w;
@@ -206,10 +215,6 @@ constexpr int kDefaultTailStepsPerTask = 2;
 constexpr int kDefaultTailSteps = 4;
 int default_steps_per_task(int64_t lk, int64_t d) { return lk * d >= (int64_t(1) << 19) ? 2 : 4; }
 
-// First step of step group g (as the kernel's group_first).
-int group_first_host(const mkra::KernelArgs& a, int g) {
-  return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group;
-}
 
 // Largest divisor of g that divides the wave count: query heads per unit.
 int heads_per_unit(int g) {
@@ -249,12 +254,99 @@ mk_status check_device_pointer(const void* p, int dev, const char* name) {
   return MK_OK;
 }
 
+// The unfused baseline of the mKernel paper's Figure 1(b): two streams, every chunk
+// released at a kernel boundary. For each ring step t, the copy stream runs a
+// staging-only launch of the ring kernel (copy_wgs workgroups, the step's tiles into
+// slot t mod kSlots, after waiting for the compute launch of step t - kSlots that last
+// read that slot), and the compute stream, after waiting for that staging launch, runs
+// a compute-only launch over every unit's step t (the remaining workgroups; the running
+// state goes through the workspace between the steps). Both use the kernel's own device
+// code; the staging launches have their own control block, since they run beside the
+// compute launches. `a` holds the fused decomposition; all launches share its epoch.
+mk_status launch_unfused(const mkra::KernelArgs& a, Workspace* w, hipStream_t stream, hipStream_t copy_stream,
+                         int copy_wgs, int64_t n_units) {
+  hipError_t e;
+  if (w->ctrl_copy == nullptr) {
+    if ((e = hipMalloc(reinterpret_cast<void**>(&w->ctrl_copy), sizeof(DevCtrl))) != hipSuccess)
+      return hip_fail(e, "workspace allocation");
+    if ((e = hipMalloc(reinterpret_cast<void**>(&w->status_copy), sizeof(DevStatus))) != hipSuccess)
+      return hip_fail(e, "workspace allocation");
+    if ((e = hipMemsetAsync(w->ctrl_copy, 0, sizeof(DevCtrl), stream)) != hipSuccess) return hip_fail(e, "memset");
+    if ((e = hipMemsetAsync(w->status_copy, 0, sizeof(DevStatus), stream)) != hipSuccess)
+      return hip_fail(e, "memset");
+  }
+  const int n_steps = a.n_steps;
+  while ((int)w->ev_staged.size() < n_steps) {
+    hipEvent_t e1, e2;
+    if ((e = hipEventCreateWithFlags(&e1, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "event");
+    if ((e = hipEventCreateWithFlags(&e2, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "event");
+    w->ev_staged.push_back(e1);
+    w->ev_computed.push_back(e2);
+  }
+  // Workgroups: copy_wgs stage; the rest of the grid computes (both resident at once).
+  const int grid_all = a.grid;
+  const int n_copy = std::max(1, std::min(copy_wgs, grid_all > 1 ? grid_all - 1 : 1));
+  const int n_comp = std::max(1, (int)std::min<int64_t>(grid_all - n_copy, n_units));
+
+  mkra::KernelArgs st = a;  // staging launches
+  st.grid = n_copy;
+  st.n_xcd = 1;
+  for (int x = 0; x <= mkra::kMaxXcd; ++x) st.xcd_unit_begin[x] = 0;
+  st.n_groups = 0;  // no compute task
+  st.n_stage_tasks = a.n_tiles;
+  st.split_fixed = 1;
+  st.initial_stagers = n_copy;
+  st.disable_staging = 0;
+  st.external_order = 1;
+  st.ctrl = w->ctrl_copy;
+  st.status = w->status_copy;
+  st.trace = nullptr;
+  st.trace_cap = 0;
+
+  mkra::KernelArgs cp = a;  // compute launches: one step each
+  cp.grid = n_comp;
+  cp.n_xcd = std::min(mkra::kMaxXcd, n_comp);
+  for (int x = 0; x <= cp.n_xcd; ++x) cp.xcd_unit_begin[x] = (int)((int64_t)x * n_units / cp.n_xcd);
+  cp.group = 1;
+  cp.tail_group = 1;
+  cp.n_big = 1;
+  cp.n_groups = 1;
+  cp.n_stage_tasks = 0;
+  cp.split_fixed = 1;
+  cp.initial_stagers = 0;
+  cp.disable_staging = 1;
+  cp.external_order = 1;
+  cp.trace = nullptr;
+  cp.trace_cap = 0;
+
+  // The copy stream starts after everything enqueued on the compute stream so far
+  // (earlier calls that used the same workspace).
+  if ((e = hipEventRecord(w->ev_computed[0], stream)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = hipStreamWaitEvent(copy_stream, w->ev_computed[0], 0)) != hipSuccess) return hip_fail(e, "event wait");
+  for (int t = 0; t < n_steps; ++t) {
+    if (t >= mkra::kSlots && (e = hipStreamWaitEvent(copy_stream, w->ev_computed[t - mkra::kSlots], 0)) != hipSuccess)
+      return hip_fail(e, "event wait");
+    st.stage_lo = t * a.n_tiles;
+    if ((e = mkra_kernel_launch(&st, copy_stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+    if ((e = hipEventRecord(w->ev_staged[t], copy_stream)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(stream, w->ev_staged[t], 0)) != hipSuccess) return hip_fail(e, "event wait");
+    cp.step_lo = t;
+    if ((e = mkra_kernel_launch(&cp, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+    if ((e = hipEventRecord(w->ev_computed[t], stream)) != hipSuccess) return hip_fail(e, "event record");
+  }
+  // The compute stream's last launch follows every staging launch (it waited for the
+  // last one), so work enqueued after the call on `stream` sees the whole call done.
+  return MK_OK;
+}
+
 // no_alloc: take every piece of device state from the fixed scratch array of the
 // current device instead of the per-(device, stream) workspace, and call nothing that
 // allocates device memory.
+// copy_stream != nullptr: the unfused two-stream baseline (staging launches on
+// copy_stream with copy_wgs workgroups, one compute launch per step on stream).
 mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, int causal, int gqa, mk_tensor* out,
               mk_tensor* lse, hipStream_t stream, const mk_ring_attn_opts* user_opts, mk_ring_attn_stats* stats,
-              bool no_alloc = false) {
+              bool no_alloc = false, hipStream_t copy_stream = nullptr, int copy_wgs = 0) {
   g_last_error.clear();
   mk_ring_attn_opts opts;
   mk_ring_attn_default_opts(&opts);
@@ -391,10 +483,10 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
       // Eq. (2) as the paper states it: every compute task remains.
       init = eq2_target_host(grid, n_units * (int64_t)n_steps, n_stage_tasks, a.cost_compute0, a.cost_stage0);
     else
-      // As on the device: R_p without the last step group, which follows the last
+      // As on the device: R_p without the last ring step, which follows the last
       // staging task whatever the split.
-      init = eq2_target_host(grid, n_units * (int64_t)group_first_host(a, a.n_groups - 1), n_stage_tasks,
-                             a.cost_compute0, a.cost_stage0);
+      init = eq2_target_host(grid, n_units * (int64_t)(n_steps - 1), n_stage_tasks, a.cost_compute0,
+                             a.cost_stage0);
   }
   a.initial_stagers = init;
   a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;
@@ -499,6 +591,8 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
       return hip_fail(e, "hipMemcpy");
   }
 
+  if (copy_stream != nullptr) return launch_unfused(a, w, stream, copy_stream, copy_wgs, n_units);
+
   if ((e = mkra_kernel_launch(&a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
 
   if (stats != nullptr) {
@@ -562,6 +656,17 @@ mk_status mk_ring_attn_fwd_noalloc(const mk_tensor* q, const mk_tensor* kv_chunk
   return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, nullptr, nullptr, true);
 }
 
+mk_status mk_ring_attn_fwd_unfused(const mk_tensor* q, const mk_tensor* kv_chunks, int n_chunks, int rank, int causal,
+                                   int gqa_ratio, mk_tensor* out, mk_tensor* lse, hipStream_t stream,
+                                   hipStream_t copy_stream, int copy_wgs) {
+  g_last_error.clear();
+  if (copy_stream == nullptr || copy_stream == stream)
+    return fail(MK_E_INVAL, "the unfused baseline needs a copy stream other than the compute stream");
+  if (copy_wgs < 1) return fail(MK_E_INVAL, "copy_wgs must be >= 1");
+  return run(q, kv_chunks, n_chunks, rank, causal, gqa_ratio, out, lse, stream, nullptr, nullptr, false, copy_stream,
+             copy_wgs);
+}
+
 mk_status mk_ring_attn_status(hipStream_t stream) {
   g_last_error.clear();
   int dev = 0;
@@ -571,9 +676,12 @@ mk_status mk_ring_attn_status(hipStream_t stream) {
   if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   // The stream's workspace, and the device's scratch array of the no-allocation entry
   // point if it has been used.
-  DevStatus* words[2] = {nullptr, nullptr};
+  DevStatus* words[3] = {nullptr, nullptr, nullptr};
   Workspace* w = find_ws(dev, stream, false);
-  if (w != nullptr) words[0] = w->status;
+  if (w != nullptr) {
+    words[0] = w->status;
+    words[2] = w->status_copy;
+  }
   if ((int)g_scratch.size() > dev && g_scratch[dev].ready) {
     void* base = nullptr;
     if ((e = mkra_scratch_address(dev, &base)) != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");

@@ -140,7 +140,11 @@ struct KernelArgs {
   int group;              // ring steps of each of the first n_big step groups, 1..kMaxGroup
   int n_big;              // step groups of `group` steps
   int tail_group;         // ring steps of each later step group, 1..group
-  int n_groups;           // step groups: compute tasks per unit
+  int n_groups;           // step groups: compute tasks per unit in this launch
+  int step_lo;            // first ring step of this launch's step groups (0 when fused)
+  int stage_lo;           // first staging task of this launch (0 when fused)
+  int external_order;     // 1: launches ordered by stream events (the unfused two-stream
+                          // baseline): staging does not wait for slot release
   float scale_log2;       // log2(e) / sqrt(D)
 
   // Decomposition into compute units: a unit is (KV head, group of HG query heads

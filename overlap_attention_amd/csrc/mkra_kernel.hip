@@ -169,9 +169,15 @@ __device__ __forceinline__ int64_t units_in_queue(const KA& a, int x) {
 // Step groups: the first n_big groups have `group` steps each, the later ones (the
 // tail) `tail_group` steps each, the last one possibly fewer. First step of group g,
 // and one past its last.
+// A launch's step groups start at ring step step_lo (0 unless the launch runs one
+// step of the unfused baseline).
+template <class KA>
+__device__ __forceinline__ int group_rel_first(const KA& a, int g) {
+  return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group;
+}
 template <class KA>
 __device__ __forceinline__ int group_first(const KA& a, int g) {
-  return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group;
+  return a.step_lo + group_rel_first(a, g);
 }
 template <class KA>
 __device__ __forceinline__ int group_end(const KA& a, int g) {
@@ -182,10 +188,10 @@ __device__ __forceinline__ int group_end(const KA& a, int g) {
 // group-major).
 template <class KA>
 __device__ __forceinline__ int64_t steps_claimed(const KA& a, int64_t ux, int64_t h) {
-  if (h >= ux * a.n_groups) return ux * a.n_steps;
+  if (h >= ux * a.n_groups) return ux * (a.n_steps - a.step_lo);
   const int g = (int)(h / ux);
-  const int f = group_first(a, g);
-  return ux * f + (h % ux) * (group_end(a, g) - f);
+  const int f = group_rel_first(a, g);
+  return ux * f + (h % ux) * (group_end(a, g) - a.step_lo - f);
 }
 
 // Run by one lane, from a snapshot of the queue heads and the staging head. Compute
@@ -229,11 +235,11 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   } else {
     cp = (int64_t)((ct + kc * (uint64_t)a.cost_compute0) / (cd + kc));
     cs = (int64_t)((stt + ks * (uint64_t)a.cost_stage0) / (sd + ks));
-    // R_p counts the compute work that can overlap the remaining staging: every task
-    // of the last step group needs that group's staged tiles, so its unit-steps follow
-    // the last staging task whatever the split, and Eq. (2) balances the rest.
-    const int64_t last_group = (int64_t)a.n_units * (a.n_steps - group_first(a, a.n_groups - 1));
-    rp2 = rp > last_group ? rp - last_group : 0;
+    // R_p counts the compute work that can overlap the remaining staging: every
+    // unit-step of the last ring step needs that step's staged tiles, so it follows the
+    // last staging task whatever the split, and Eq. (2) balances the rest.
+    const int64_t last_step = (int64_t)a.n_units;
+    rp2 = rp > last_step ? rp - last_step : 0;
   }
   if (cp < 1) cp = 1;
   if (cs < 1) cs = 1;
@@ -421,7 +427,7 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
   const int slot = t % kSlots;
   uint64_t w = 0;
   // Slot release (every wave waits; a timeout leaves the error word set for all).
-  if (t >= kSlots) wave_wait_ge32(a, &a.done_count[t - kSlots], (uint32_t)a.n_units, w);
+  if (t >= kSlots && !a.external_order) wave_wait_ge32(a, &a.done_count[t - kSlots], (uint32_t)a.n_units, w);
   // One verdict for the whole workgroup (the barriers below are inside the branch).
   const bool ok = __syncthreads_or(has_error(a) ? 1 : 0) == 0;
   bool v_range = false;  // some V of the tile does not fit the fp16 PV operand
@@ -1370,7 +1376,7 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     int released_below = 0;  // steps whose slot is known released
     const int pend_last = group_end(a, st->pend_g) - 1;  // last step the task runs
     for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
-      const int step = (int)h / a.n_tiles;
+      const int step = (a.stage_lo + (int)h) / a.n_tiles;
       if (step > pend_last) break;
       if (step >= kSlots && step >= released_below) {
         if (ld32(&a.done_count[step - kSlots]) < (uint32_t)a.n_units) break;
@@ -1460,7 +1466,7 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
             trace_rec(ap, kTraceCompute, x, t, (int64_t)t0, (int64_t)w0, 0, 0);
       }
     } else {
-      stage_tile<D>(a, ap, (uint32_t)x, y != 0);
+      stage_tile<D>(a, ap, (uint32_t)(a.stage_lo + x), y != 0);
     }
   }
 
@@ -1506,7 +1512,10 @@ __global__ __launch_bounds__(kThreads) void ring_attn_kernel(KernelArgs a) {
   __syncthreads();
   uint32_t* words = reinterpret_cast<uint32_t*>(cb);
   for (int i = tid; i < (int)(sizeof(DevCtrl) / 4); i += kThreads) words[i] = 0;
-  for (int i = tid; i < a.n_steps; i += kThreads) a.done_count[i] = 0;
+  // (A staging-only launch of the unfused baseline leaves the counters to the compute
+  // launches that run beside it.)
+  if (a.n_groups > 0)
+    for (int i = tid; i < a.n_steps; i += kThreads) a.done_count[i] = 0;
 }
 
 template __global__ void ring_attn_kernel<64>(KernelArgs);

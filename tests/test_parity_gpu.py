@@ -233,6 +233,12 @@ def test_bitwise_identical_across_splits_grids_and_delays():
     variants += [dict(stage_delay_ticks=2000), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
                                                    stage_delay_ticks=5000)]
     variants += [dict(initial_staging_wgs=16, controller_period_us=1)]
+    # Task sizes and tails: the blocks of a unit are processed in the same order with the
+    # same arithmetic whatever the grouping (the state between tasks is stored and
+    # reloaded exactly), so the results do not change either.
+    variants += [dict(steps_per_task=g, tail_steps=-1) for g in (1, 2, 3, 4)]
+    variants += [dict(steps_per_task=4, tail_steps=2, tail_steps_per_task=1),
+                 dict(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)]
     for v in variants:
         announce(f"variant {v}")
         o, l = run_gpu(qg, kvg, cfg, **v)
@@ -310,7 +316,7 @@ def group_firsts(n_steps, g, tail_steps, tail_g):
                          ids=["adaptive-g4", "paper-g4", "adaptive-g2", "adaptive-g3-tail2x1"])
 def test_stats_and_controller_follow_eq2(mode, groups):
     """Every controller update of a traced run sets the target Eq. (2) gives for the
-    inputs it records. ADAPTIVE: R_p leaves out the last step group's unit-steps.
+    inputs it records. ADAPTIVE: R_p leaves out the last ring step's unit-steps.
     ADAPTIVE_PAPER: R_p is every unclaimed unit-step, and C_p, C_s are plain measured
     averages; the first update's R_p then equals the whole compute work minus what
     was claimed before it."""
@@ -331,13 +337,13 @@ def test_stats_and_controller_follow_eq2(mode, groups):
     stage = [r for r in recs if r[2] == 2]
     assert len(comp) == st["compute_tasks_done"] and len(stage) == st["staging_tasks_done"]
     assert len(ctrl) == st["controller_updates"] and len(ctrl) >= 1
-    # R_p as Eq. (2) takes it: unclaimed unit-steps, outside the last step group in
+    # R_p as Eq. (2) takes it: unclaimed unit-steps, less the last ring step's in
     # ADAPTIVE mode (those follow the last staging task whatever the split).
     # This workload's units fit the grid, so the default tail is none; explicit tails
     # follow the documented rule.
     firsts = group_firsts(st["n_steps"], g, max(tail_steps, 0), tail_g)
     assert st["steps_per_task"] == g and st["step_groups"] == len(firsts), (st, firsts)
-    rp_max = st["n_units"] * (firsts[-1] if mode == "adaptive" else st["n_steps"])
+    rp_max = st["n_units"] * (st["n_steps"] - 1 if mode == "adaptive" else st["n_steps"])
     for r in ctrl:
         rp, rs, cp, cs, b, target = r[3:9]
         assert 0 <= rp <= rp_max, (r, rp_max)
