@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for the per-rank ring-attention forward.
+"""Plain fp64 CPU oracles for the per-rank ring-attention forward and for one rank's
+AllGather+GEMM.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this package.
@@ -18,8 +19,14 @@ Sources (the web pages on mKernel, cited by page title and section):
   print no attention formula; the definition used here is the standard scaled
   dot-product softmax attention those works compute, written out in full.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against brute force,
-closed forms and invariants; none is "parity unpinned".
+- For AllGather+GEMM: the same paper, §4 and Table 3 (AllGather + GEMM row: shards
+  moved in 128-row chunks, compute consumes them as they arrive, local shard first),
+  and the README's kernel table (AllGather + GEMM row). The definition is the plain
+  product of the gathered activation with the rank's weight shard.
+
+Every function is pinned against brute force, closed forms and invariants
+(``tests/test_oracle_pins.py``, ``tests/test_oracle_allgather_gemm.py``); none is
+"parity unpinned".
 """
 
 from .ring_attention import (  # noqa: F401
@@ -29,4 +36,11 @@ from .ring_attention import (  # noqa: F401
     staging_tiles,
     controller_target,
     attention_flops,
+)
+from .allgather_gemm import (  # noqa: F401
+    A_CHUNK_ROWS,
+    allgather,
+    allgather_gemm_reference,
+    allgather_schedule,
+    gemm_flops,
 )
