@@ -1,11 +1,17 @@
-"""MI355X-native per-rank ring-attention forward (mKernel's Ring Attention, one rank).
+"""MI355X-native per-rank ring-attention forward (mKernel's Ring Attention, one rank)
+and one rank's AllGather+GEMM on the same persistent-kernel runtime.
 
-The computation lives in the HIP library libmkra.so (C ABI in include/mkra.h); this
-package is its Python binding. Build the library with
+The computation lives in the HIP library libmkra.so (C ABI in include/mkra.h and
+include/mkag.h); this package is its Python binding. Build the library with
 ``python -m overlap_attention_amd.build``.
 """
 
 from ._binding import (  # noqa: F401
+    ag_default_opts,
+    allgather_gemm,
+    mk_ag_gemm_status,
+    mk_allgather_gemm,
+    mk_allgather_gemm_ex,
     LIB_PATH,
     MK_BF16,
     MK_E_HIP,

@@ -83,6 +83,42 @@ class mk_ring_attn_stats(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_ if not name.startswith("reserved")}
 
 
+class mk_ag_gemm_opts(ctypes.Structure):
+    _fields_ = [
+        ("split_mode", ctypes.c_int32),
+        ("fixed_staging_wgs", ctypes.c_int32),
+        ("initial_staging_wgs", ctypes.c_int32),
+        ("grid_wgs", ctypes.c_int32),
+        ("spin_timeout_us", ctypes.c_int64),
+        ("controller_period_us", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
+    ]
+
+
+class mk_ag_gemm_stats(ctypes.Structure):
+    _fields_ = [
+        ("status", ctypes.c_int32),
+        ("grid_wgs", ctypes.c_int32),
+        ("compute_tiles", ctypes.c_int32),
+        ("staging_tasks", ctypes.c_int32),
+        ("compute_done", ctypes.c_int32),
+        ("staging_done", ctypes.c_int32),
+        ("assist_tasks", ctypes.c_int32),
+        ("controller_updates", ctypes.c_int32),
+        ("max_staging_wgs", ctypes.c_int32),
+        ("final_target", ctypes.c_int32),
+        ("compute_busy_ticks", ctypes.c_int64),
+        ("compute_wait_ticks", ctypes.c_int64),
+        ("staging_busy_ticks", ctypes.c_int64),
+        ("kernel_ticks", ctypes.c_int64),
+        ("wg_cycles", ctypes.c_int64),
+        ("wg_ticks", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class mk_trace_record(ctypes.Structure):
     _fields_ = [("t", ctypes.c_uint64), ("wg", ctypes.c_int32), ("kind", ctypes.c_int32), ("v", ctypes.c_int64 * 6)]
 
@@ -107,6 +143,15 @@ _PROTOTYPES = {
     "mk_ring_attn_status": (ctypes.c_int, [ctypes.c_void_p]),
     "mk_ring_attn_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(mk_trace_record), ctypes.c_int64,
                                           ctypes.POINTER(ctypes.c_int64)]),
+    "mk_allgather_gemm": (ctypes.c_int, [ctypes.POINTER(mk_tensor), ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(mk_tensor), ctypes.POINTER(mk_tensor),
+                                         ctypes.POINTER(mk_tensor), ctypes.c_void_p]),
+    "mk_allgather_gemm_ex": (ctypes.c_int, [ctypes.POINTER(mk_tensor), ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(mk_tensor), ctypes.POINTER(mk_tensor),
+                                            ctypes.POINTER(mk_tensor), ctypes.c_void_p,
+                                            ctypes.POINTER(mk_ag_gemm_opts), ctypes.POINTER(mk_ag_gemm_stats)]),
+    "mk_ag_gemm_default_opts": (None, [ctypes.POINTER(mk_ag_gemm_opts)]),
+    "mk_ag_gemm_status": (ctypes.c_int, [ctypes.c_void_p]),
     "mk_last_error": (ctypes.c_char_p, []),
     "mk_release_workspace": (None, []),
     "mk_abi_version": (ctypes.c_int, []),
@@ -257,3 +302,55 @@ def ring_attn_fwd(q, kv_chunks, rank: int, causal: bool, gqa_ratio: int, opts: O
     stats = mk_ring_attn_fwd_ex(q, kv_chunks, kv_chunks.shape[0], rank, causal, gqa_ratio, out, lse, stream=stream,
                                 opts=opts, want_stats=want_stats)
     return (out, lse, stats) if want_stats else (out, lse)
+
+
+# ------------------------------------------------------------------ AllGather+GEMM
+
+def ag_default_opts(**overrides) -> mk_ag_gemm_opts:
+    o = mk_ag_gemm_opts()
+    load_library().mk_ag_gemm_default_opts(ctypes.byref(o))
+    for k, v in overrides.items():
+        if not hasattr(o, k):
+            raise KeyError(k)
+        setattr(o, k, v)
+    return o
+
+
+def mk_allgather_gemm(a_shards, n_ranks: int, rank: int, w, a_full, c, stream=None) -> None:
+    """Thin call of mk_allgather_gemm on torch tensors (all on the current GPU)."""
+    lib = load_library()
+    ad, wd, fd, cd = tensor_desc(a_shards), tensor_desc(w), tensor_desc(a_full), tensor_desc(c)
+    _check(lib.mk_allgather_gemm(ctypes.byref(ad), n_ranks, rank, ctypes.byref(wd), ctypes.byref(fd),
+                                 ctypes.byref(cd), _stream_ptr(stream)))
+
+
+def mk_allgather_gemm_ex(a_shards, n_ranks: int, rank: int, w, a_full, c, stream=None,
+                         opts: Optional[mk_ag_gemm_opts] = None, want_stats: bool = False):
+    """Thin call of mk_allgather_gemm_ex; returns the stats dict when want_stats."""
+    lib = load_library()
+    ad, wd, fd, cd = tensor_desc(a_shards), tensor_desc(w), tensor_desc(a_full), tensor_desc(c)
+    st = mk_ag_gemm_stats() if want_stats else None
+    _check(lib.mk_allgather_gemm_ex(ctypes.byref(ad), n_ranks, rank, ctypes.byref(wd), ctypes.byref(fd),
+                                    ctypes.byref(cd), _stream_ptr(stream),
+                                    ctypes.byref(opts) if opts is not None else None,
+                                    ctypes.byref(st) if st is not None else None))
+    return st.as_dict() if st is not None else None
+
+
+def mk_ag_gemm_status(stream=None) -> int:
+    """Status of earlier AllGather+GEMM calls on the stream; raises MkError unless MK_OK."""
+    _check(load_library().mk_ag_gemm_status(_stream_ptr(stream)))
+    return MK_OK
+
+
+def allgather_gemm(a_shards, rank: int, w, opts: Optional[mk_ag_gemm_opts] = None, want_stats: bool = False,
+                   stream=None) -> Tuple:
+    """Allocates a_full [N*M_loc, K] and c [N*M_loc, N_out] (bf16) and runs one rank's
+    AllGather+GEMM. Returns (a_full, c) or (a_full, c, stats) when want_stats."""
+    import torch
+
+    n, m_loc, k = a_shards.shape
+    a_full = torch.empty((n * m_loc, k), dtype=a_shards.dtype, device=a_shards.device)
+    c = torch.empty((n * m_loc, w.shape[0]), dtype=a_shards.dtype, device=a_shards.device)
+    stats = mk_allgather_gemm_ex(a_shards, n, rank, w, a_full, c, stream=stream, opts=opts, want_stats=want_stats)
+    return (a_full, c, stats) if want_stats else (a_full, c)

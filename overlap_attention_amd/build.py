@@ -1,5 +1,6 @@
 """Builds the in-tree HIP libraries for gfx950: overlap_attention_amd/libmkra.so (the
-ring-attention path) and libmkra_probes.so (measurement probes that bench.py runs).
+ring-attention path and the AllGather+GEMM path) and libmkra_probes.so (measurement
+probes that bench.py runs).
 
 Usage: python -m overlap_attention_amd.build   (or overlap_attention_amd.build.build())
 """
@@ -11,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmkra.so")
-SOURCES = [os.path.join(HERE, "csrc", "mkra_kernel.hip"), os.path.join(HERE, "csrc", "mkra_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("mkra_kernel.hip", "mkra_api.cpp", "mkag_kernel.hip", "mkag_api.cpp")]
+KERNEL_SOURCES = [SOURCES[0], SOURCES[2]]
 PROBES_LIB = os.path.join(HERE, "libmkra_probes.so")
 PROBES_SOURCES = [os.path.join(HERE, "csrc", "mkra_probes.hip")]
 

@@ -632,6 +632,11 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
 
 }  // namespace
 
+// The AllGather+GEMM layer (mkag_api.cpp) reports through the same last-error
+// message and frees its workspaces with the others.
+extern "C" __attribute__((visibility("hidden"))) void mkra_set_last_error(const char* msg) { g_last_error = msg; }
+extern "C" __attribute__((visibility("hidden"))) void mkag_release_workspaces(void);
+
 extern "C" {
 
 void mk_ring_attn_default_opts(mk_ring_attn_opts* opts) {
@@ -729,9 +734,12 @@ mk_status mk_ring_attn_trace(hipStream_t stream, mk_trace_record* records, int64
 const char* mk_last_error(void) { return g_last_error.c_str(); }
 
 void mk_release_workspace(void) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  for (Workspace* w : g_ws) free_ws(w);
-  g_ws.clear();
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (Workspace* w : g_ws) free_ws(w);
+    g_ws.clear();
+  }
+  mkag_release_workspaces();
 }
 
 int mk_abi_version(void) { return MKRA_ABI_VERSION; }

@@ -53,6 +53,24 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref):
     return rep
 
 
+def compare_gemm(c_gpu, c_ref, abs_sum, k):
+    """GEMM outputs (bf16, fp32 accumulation over K) against the fp64 product.
+
+    Per element the bar is half a bf16 ulp of the exact value (the final rounding) plus
+    the standard bound of an fp32 accumulation, gamma_n * sum_k |a_k w_k| with
+    gamma_n = n * 2^-24 and n = K/16 + 16 (K/16 accumulating MFMA steps, each summing 16
+    products). abs_sum is sum_k |a_k w_k| per element. Returns a report dict;
+    report['ok'] is the verdict, 'worst_over_bar' the largest error / bar ratio."""
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c_gpu - c_ref)
+    n = k / 16 + 16
+    bar = np.where(c_ref != 0, bf16_half_ulp(c_ref), 0.0) + n * 2.0 ** -24 * abs_sum
+    rep = {"finite": bool(np.isfinite(c_gpu).all()), "max_abs_err": float(err.max()) if err.size else 0.0,
+           "worst_over_bar": float((err / np.maximum(bar, 1e-300)).max()) if err.size else 0.0}
+    rep["ok"] = rep["finite"] and bool((err <= bar).all())
+    return rep
+
+
 def oracle_rows(oracle_mod, q64, kv64, rank, causal, gqa_ratio, rows=None, workers=None, progress=False):
     """The oracle's definition evaluated one KV head at a time, the heads spread over
     threads (query heads of different KV heads never interact, so each KV head with its
@@ -110,5 +128,5 @@ def fmt(rep):
     return ", ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}" for k, v in rep.items())
 
 
-__all__ = ["compare", "sample_rows", "wave_slice_rows", "oracle_rows", "fmt", "OUT_ATOL", "LSE_RTOL",
+__all__ = ["compare", "compare_gemm", "sample_rows", "wave_slice_rows", "oracle_rows", "fmt", "OUT_ATOL", "LSE_RTOL",
            "bf16_half_ulp", "math"]

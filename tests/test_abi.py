@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every entry point include/mkra.h declares, and
+"""The C-ABI library loads, exports every entry point include/*.h declares, and
 rejects bad arguments on the host before touching a GPU. Runs without a GPU."""
 
 import ctypes
@@ -13,18 +13,21 @@ import overlap_attention_amd as mk
 from overlap_attention_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mkra.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(mk_\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(mk_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_header_lists_the_entry_points():
     names = declared_functions()
-    assert "mk_ring_attn_fwd" in names and "mk_ring_attn_fwd_ex" in names
+    assert "mk_ring_attn_fwd" in names and "mk_ring_attn_fwd_ex" in names and "mk_allgather_gemm" in names
     assert set(names) == set(B._PROTOTYPES), names
 
 
@@ -63,13 +66,15 @@ def test_struct_layouts_match_the_header():
     prog = r'''
 #include <stdio.h>
 #include <stddef.h>
-#include "mkra.h"
+#include "mkag.h"
 int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(mk_tensor), sizeof(mk_ring_attn_opts), sizeof(mk_ring_attn_stats),
          sizeof(mk_trace_record));
   printf("%zu %zu %zu %zu %zu %zu\n", offsetof(mk_ring_attn_opts, spin_timeout_us), offsetof(mk_ring_attn_opts, trace),
          offsetof(mk_ring_attn_stats, compute_busy_ticks), offsetof(mk_ring_attn_stats, trace_records),
          offsetof(mk_ring_attn_opts, debug_flags), offsetof(mk_ring_attn_stats, debug_mismatches));
+  printf("%zu %zu %zu %zu\n", sizeof(mk_ag_gemm_opts), sizeof(mk_ag_gemm_stats),
+         offsetof(mk_ag_gemm_opts, spin_timeout_us), offsetof(mk_ag_gemm_stats, compute_busy_ticks));
   return 0;
 }
 '''
@@ -81,7 +86,7 @@ int main(void) {
                             "-I/opt/rocm/include", c, "-o", exe], capture_output=True, text=True)
         if r.returncode != 0:
             pytest.skip("no C compiler for the layout check: " + r.stderr[-300:])
-        sizes, offs = subprocess.run([exe], capture_output=True, text=True).stdout.split("\n")[:2]
+        sizes, offs, ag = subprocess.run([exe], capture_output=True, text=True).stdout.split("\n")[:3]
     assert [int(x) for x in sizes.split()] == [ctypes.sizeof(B.mk_tensor), ctypes.sizeof(B.mk_ring_attn_opts),
                                                ctypes.sizeof(B.mk_ring_attn_stats),
                                                ctypes.sizeof(B.mk_trace_record)]
@@ -91,6 +96,9 @@ int main(void) {
                                               B.mk_ring_attn_stats.trace_records.offset,
                                               B.mk_ring_attn_opts.debug_flags.offset,
                                               B.mk_ring_attn_stats.debug_mismatches.offset]
+    assert [int(x) for x in ag.split()] == [ctypes.sizeof(B.mk_ag_gemm_opts), ctypes.sizeof(B.mk_ag_gemm_stats),
+                                            B.mk_ag_gemm_opts.spin_timeout_us.offset,
+                                            B.mk_ag_gemm_stats.compute_busy_ticks.offset]
 
 
 def test_default_opts():
@@ -209,9 +217,9 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), f
-                assert "ring_attention_reference" not in src, f
+                assert "ring_attention_reference" not in src and "allgather_gemm_reference" not in src, f
     oracle_dir = os.path.join(ROOT, "oracle")
     for f in os.listdir(oracle_dir):
         if f.endswith(".py"):
             src = open(os.path.join(oracle_dir, f)).read()
-            assert "overlap_attention_amd" not in src and "ring_inputs" not in src, f
+            assert "overlap_attention_amd" not in src and "ring_inputs" not in src and "ag_inputs" not in src, f

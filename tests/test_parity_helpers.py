@@ -33,3 +33,20 @@ def test_strict_figures_reported():
     # an lse of 0.5 off by 6e-4 passes the floored bar but is 1.2e-3 relative.
     assert rep["ok"] and rep["out_strict_over"] == 1
     assert abs(rep["lse_max_rel_err_strict"] - 1.2e-3) < 1e-12
+
+
+def test_gemm_bar_accepts_rounding_and_rejects_a_wrong_term():
+    from tests.parity import compare_gemm
+
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((8, 64))
+    w = rng.standard_normal((16, 64))
+    ref = a @ w.T
+    abs_sum = np.abs(a) @ np.abs(w).T
+    # the exact product rounded to bf16 passes
+    rounded = np.array(ref, dtype=np.float32).view(np.uint32)
+    rounded = ((rounded + 0x7FFF + ((rounded >> 16) & 1)) & 0xFFFF0000).view(np.float32).astype(np.float64)
+    assert compare_gemm(rounded, ref, abs_sum, 64)["ok"]
+    # dropping one k term does not
+    wrong = a[:, :-1] @ w[:, :-1].T
+    assert not compare_gemm(wrong, ref, abs_sum, 64)["ok"]
