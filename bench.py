@@ -320,6 +320,109 @@ def run_unfused_sweep(torch, mk, make_inputs, stream, sizes=SWEEP_SIZES):
     return rows
 
 
+AG_METRIC = "AllGather+GEMM TFLOP/s and % bf16 MFMA peak, one rank of a tensor-parallel group, 1 MI355X"
+AG_SIZES = (4096, 8192, 16384, 32768)
+
+
+def run_ag(args):
+    """One rank's AllGather+GEMM (C = A_full W^T after gathering the shards): the fused
+    persistent kernel against the unfused baseline (the gather as one device copy, then
+    the library GEMM, torch.matmul on hipBLASLt, on the same stream), over the gathered
+    sizes of Figure 4 (4K-32K rows, 8 ranks, K 8192, N 4096), with a staging split sweep
+    on the named workload. Prints one JSON line."""
+    import torch
+
+    import overlap_attention_amd as mk
+    from ag_inputs import AG_CONFIG_BY_NAME, AG_CONFIGS, ag_sweep_config, make_ag_inputs
+
+    cfg = AG_CONFIG_BY_NAME[args.ag_workload] if args.ag_workload else AG_CONFIGS[1]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def setup(c):
+        a, w = make_ag_inputs(c, seed=1)
+        a, w = a.cuda(), w.cuda()
+        a_full = torch.empty((c.m, c.k), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((c.m, c.n_out), dtype=torch.bfloat16, device="cuda")
+        return a, w, a_full, out
+
+    def timed(fn, k):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(k):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / k
+
+    def fused_fn(c, a, w, a_full, out, o=None):
+        return lambda: mk.mk_allgather_gemm_ex(a, c.n_ranks, c.rank, w, a_full, out, stream=stream, opts=o)
+
+    def unfused_fn(c, a, w, a_full, out):
+        def f():
+            a_full.copy_(a.reshape(c.m, c.k))
+            torch.matmul(a_full, w.t(), out=out)
+        return f
+
+    a, w, a_full, out = setup(cfg)
+    flops = 2 * cfg.m * cfg.n_out * cfg.k
+    ms = timed(fused_fn(cfg, a, w, a_full, out), args.steps)
+    mk.mk_ag_gemm_status(stream)
+    st = mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, a_full, out, stream=stream, want_stats=True)
+    ms_unf = timed(unfused_fn(cfg, a, w, a_full, out), args.steps)
+    tflops = flops / (ms * 1e-3) / 1e12
+    clock = st["wg_cycles"] / st["wg_ticks"] * 0.1 if st["wg_ticks"] else None
+    log(f"[bench] ag {cfg.name}: fused {ms:.4f} ms ({tflops:.1f} TFLOP/s), unfused {ms_unf:.4f} ms, stats {st}")
+    split = {}
+    for n in (1, 2, 4, 8, 16, 32):
+        split[f"fixed{n}"] = round(timed(fused_fn(cfg, a, w, a_full, out, mk.ag_default_opts(
+            split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n)), max(3, args.steps // 3)), 4)
+    split["adaptive"] = round(ms, 4)
+    split["adaptive_paper"] = round(timed(fused_fn(cfg, a, w, a_full, out, mk.ag_default_opts(
+        split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)), max(3, args.steps // 3)), 4)
+    best = min((k for k in split if k.startswith("fixed")), key=split.get)
+    log("[bench] ag split sweep: " + ", ".join(f"{k}={v:.3f}" for k, v in split.items()))
+    del a, w, a_full, out
+    torch.cuda.empty_cache()
+    sweep = []
+    if args.ag_sweep:
+        for m in AG_SIZES:
+            c = ag_sweep_config(m)
+            a, w, a_full, out = setup(c)
+            f = 2 * c.m * c.n_out * c.k
+            k = max(5, min(50, int(20 / (m / 16384))))
+            t_f = timed(fused_fn(c, a, w, a_full, out), k)
+            t_u = timed(unfused_fn(c, a, w, a_full, out), k)
+            mk.mk_ag_gemm_status(stream)
+            sweep.append({"m": m, "fused_ms": round(t_f, 4), "unfused_ms": round(t_u, 4),
+                          "unfused_over_fused": round(t_u / t_f, 3), "fused_tflops": round(f / t_f / 1e9, 1),
+                          "unfused_tflops": round(f / t_u / 1e9, 1)})
+            log(f"[bench] ag M={m}: fused {t_f:.4f} ms ({f / t_f / 1e9:.1f} TFLOP/s), unfused {t_u:.4f} ms "
+                f"({f / t_u / 1e9:.1f} TFLOP/s), unfused/fused {t_u / t_f:.3f}")
+            del a, w, a_full, out
+            torch.cuda.empty_cache()
+    line = {
+        "metric": AG_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, **cfg.as_dict(), "algorithmic_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "kernel": "mkag::ag_gemm_kernel",
+                     "shader_clock_ghz": round(clock, 3) if clock else None},
+        "unfused_baseline": {"what": "device copy of the shards into A_full, then torch.matmul (hipBLASLt)",
+                             "ms": round(ms_unf, 4), "unfused_over_fused": round(ms_unf / ms, 3)},
+        "split_sweep": {"ms": split, "best_fixed": best, "adaptive_over_best": round(split["adaptive"] / split[best], 3),
+                        "adaptive_paper_over_best": round(split["adaptive_paper"] / split[best], 3)},
+        "staging": {k: st[k] for k in ("grid_wgs", "staging_tasks", "assist_tasks", "max_staging_wgs")},
+    }
+    if sweep:
+        line["size_sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
 PROBE_MODES = (
     (2, "MFMA + ds_read_b128, random bf16"),
     (0, "MFMA, random bf16 from registers"),
@@ -490,6 +593,11 @@ def main():
                          "profiles/traffic_<workload>.json")
     ap.add_argument("--probes", action="store_true",
                     help="run the MFMA-stream and vector-ALU probes instead of the benchmark; prints markdown")
+    ap.add_argument("--ag", action="store_true",
+                    help="benchmark one rank's AllGather+GEMM instead (fused kernel, unfused copy + library GEMM, "
+                         "split sweep); prints its own JSON line")
+    ap.add_argument("--ag-workload", default=None, help="name of a workload in ag_inputs.AG_CONFIGS")
+    ap.add_argument("--ag-sweep", action="store_true", help="with --ag: also sweep the gathered size 4K..32K rows")
     ap.add_argument("--cpu-all", action="store_true",
                     help="no GPU: one timed oracle pass (every row) per workload on the host cores; prints markdown")
     ap.add_argument("--kernel-stats-from", default=None,
@@ -501,6 +609,12 @@ def main():
         return
     if args.cpu_all:
         print(cpu_all_workloads(), flush=True)
+        return
+    if args.ag:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+            sys.exit(2)
+        run_ag(args)
         return
     if args.kernel_stats_from:
         print(kernel_stats_from(args.kernel_stats_from, args.warmup, args.steps), flush=True)
