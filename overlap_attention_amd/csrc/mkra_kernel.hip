@@ -523,8 +523,10 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
       while (ticks() < until) __builtin_amdgcn_s_sleep(1);
     }
   }
-  // Every wave's stores precede the barrier; one agent-scope release by thread 0
-  // then covers the whole tile (workgroup-scope order, then agent scope).
+  // Every wave waits for its own stores to complete (a workgroup-scope fence alone
+  // does not: it emits no wait before the barrier), then one agent-scope release by
+  // thread 0 covers the whole tile.
+  wait_vm(0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0) {
