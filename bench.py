@@ -348,8 +348,15 @@ def run_ag(args):
         return a, w, a_full, out
 
     def timed(fn, k):
-        for _ in range(3):
+        # Warm-up: at least `--warmup` launches and about 0.3 s of work, so the first timed
+        # region does not run at the idle clock.
+        t_end = time.perf_counter() + 0.3
+        n = 0
+        while n < max(args.warmup, 3) or time.perf_counter() < t_end:
             fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)

@@ -11,10 +11,12 @@
  * project README's kernel table (AllGather + GEMM row).
  *
  * On one GPU the call plays one rank of an N-rank tensor-parallel group. The staging
- * role plays the gather: it copies each shard's 128-row chunks from the shard's home
+ * role plays the gather: it copies each shard's 128-row chunks (as 64-row pieces, so
+ * two workgroups can share a chunk) from the shard's home
  * (a_shards[s], standing for rank s's memory) into the gathered activation a_full and
  * publishes a ready flag per chunk. The compute role computes C = A_full W^T in
- * 128 x 512 output tiles as their rows arrive, reading the local shard in place.
+ * 256 x 256 output tiles (two chunks of one shard each) as their rows arrive, reading
+ * the local shard in place.
  *
  * Conventions are those of include/mkra.h: tensor data pointers are device pointers on
  * the current HIP device, everything else host pointers; the caller owns the tensors;
@@ -53,8 +55,10 @@ typedef struct {
 typedef struct {
   int32_t status;              /* device-side result: MK_OK or MK_E_TIMEOUT */
   int32_t grid_wgs;
-  int32_t compute_tiles;       /* output tiles: N * ceil(M_loc/128) * ceil(N_out/512) */
-  int32_t staging_tasks;       /* chunks: N * ceil(M_loc/128) (the local shard's too) */
+  int32_t compute_tiles;       /* output tiles: N * ceil(M_loc/256) * ceil(N_out/256) */
+  int32_t staging_tasks;       /* 64-row pieces, 2 per 128-row chunk: N * ceil(M_loc/128)
+                                  * 2 (the local shard's too); a chunk's ready flag
+                                  counts its pieces in */
   int32_t compute_done;
   int32_t staging_done;
   int32_t assist_tasks;        /* chunks staged by compute workgroups (stall rule) */
@@ -84,7 +88,8 @@ typedef struct {
  *                            fp32 and rounded to bf16 once.
  *  stream    HIP stream the kernel is enqueued on.
  *
- * K must be a multiple of 32 and N_out a multiple of 8 (else MK_E_UNSUPPORTED); M_loc
+ * K must be a multiple of 64 (at most 2^22) and N_out a multiple of 8 (else
+ * MK_E_UNSUPPORTED, MK_E_INVAL past the bound); M_loc
  * may be any size (ragged chunks are masked). M_loc == 0 or N_out == 0 with nothing to
  * gather is a no-op. Data pointers must be 16-byte aligned; a_full and c must not
  * overlap the inputs or each other. Asynchronous; device-side timeouts are reported

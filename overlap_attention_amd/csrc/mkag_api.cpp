@@ -148,9 +148,10 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
     if (stats != nullptr) std::memset(stats, 0, sizeof(*stats));
     return MK_OK;  // nothing to gather or compute
   }
-  if (k == 0 || k % 32 != 0) return fail(MK_E_UNSUPPORTED, "K must be a positive multiple of 32");
+  if (k == 0 || k % mkag::kBK != 0) return fail(MK_E_UNSUPPORTED, "K must be a positive multiple of 64");
   if (n_out % 8 != 0) return fail(MK_E_UNSUPPORTED, "N_out must be a multiple of 8");
-  if (m_loc > (1 << 24) || k > (1 << 24) || n_out > (1 << 24) || n > 4096)
+  // K <= 2^22 keeps a lane's byte offset inside a tile (255 rows of 2K bytes) in 32 bits.
+  if (m_loc > (1 << 24) || k > (1 << 22) || n_out > (1 << 24) || n > 4096)
     return fail(MK_E_INVAL, "extent too large");
 
   mkag::Args a;
@@ -165,9 +166,11 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
   a.k = (int)k;
   a.n_out = (int)n_out;
   a.n_chunks = (int)((m_loc + mkag::kChunkRows - 1) / mkag::kChunkRows);
+  a.n_rtiles = (int)((m_loc + mkag::kBM - 1) / mkag::kBM);
   a.n_ntiles = (int)((n_out + mkag::kBN - 1) / mkag::kBN);
-  const int64_t n_stage = n * (int64_t)a.n_chunks;
-  const int64_t n_compute = n_stage * a.n_ntiles;
+  const int64_t n_flags = n * (int64_t)a.n_chunks;
+  const int64_t n_stage = n_flags * mkag::kPieces;
+  const int64_t n_compute = n * (int64_t)a.n_rtiles * a.n_ntiles;
   if (n_compute > (int64_t)INT32_MAX / 2) return fail(MK_E_INVAL, "too many output tiles");
   a.n_stage_tasks = (int)n_stage;
   a.n_compute = (int)n_compute;
@@ -208,8 +211,8 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
   // 40 GB/s per workgroup. Ticks are 100 MHz.
   const double tile_flops = 2.0 * mkag::kBM * mkag::kBN * (double)k;
   a.cost_compute0 = std::max<int64_t>(1, (int64_t)(tile_flops / (0.5 * 4096.0 * 2.4e9) * 1e8));
-  const double chunk_bytes = 2.0 * 2.0 * std::min<int64_t>(mkag::kChunkRows, m_loc) * (double)k;
-  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(chunk_bytes / 40e9 * 1e8));
+  const double piece_bytes = 2.0 * 2.0 * std::min<int64_t>(mkag::kPieceRows, m_loc) * (double)k;
+  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(piece_bytes / 40e9 * 1e8));
   a.split_fixed = opts.split_mode == MK_SPLIT_FIXED ? 1 : 0;
   a.ctrl_paper = opts.split_mode == MK_SPLIT_ADAPTIVE_PAPER ? 1 : 0;
   int init;
@@ -232,17 +235,17 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
     if ((e = hipMemsetAsync(ws->ctrl, 0, sizeof(mkag::Ctrl), stream)) != hipSuccess) return hip_fail(e, "memset");
     if ((e = hipMemsetAsync(ws->status, 0, sizeof(mkag::Status), stream)) != hipSuccess) return hip_fail(e, "memset");
   }
-  if (ws->flags == nullptr || ws->flags_cap < (size_t)n_stage) {
+  if (ws->flags == nullptr || ws->flags_cap < (size_t)n_flags) {
     if (ws->flags != nullptr) {
       if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
       hipFree(ws->flags);
       ws->flags = nullptr;
     }
-    if ((e = hipMalloc(reinterpret_cast<void**>(&ws->flags), (size_t)n_stage * sizeof(uint64_t))) != hipSuccess)
+    if ((e = hipMalloc(reinterpret_cast<void**>(&ws->flags), (size_t)n_flags * sizeof(uint64_t))) != hipSuccess)
       return hip_fail(e, "workspace allocation");
-    if ((e = hipMemsetAsync(ws->flags, 0, (size_t)n_stage * sizeof(uint64_t), stream)) != hipSuccess)
+    if ((e = hipMemsetAsync(ws->flags, 0, (size_t)n_flags * sizeof(uint64_t), stream)) != hipSuccess)
       return hip_fail(e, "memset");
-    ws->flags_cap = (size_t)n_stage;
+    ws->flags_cap = (size_t)n_flags;
   }
   a.flags = ws->flags;
   a.ctrl = ws->ctrl;

@@ -6,18 +6,27 @@
 
 namespace mkag {
 
-// A compute workgroup: 8 waves of 64 lanes, laid out 2 (rows) x 4 (columns); each wave
-// owns a 64 x 128 block of the output tile.
-constexpr int kWaves = 8;
+// A compute workgroup: 4 waves of 64 lanes, one per SIMD, laid out 2 (rows) x 2
+// (columns); each wave owns a 128 x 128 block of the output tile (its accumulators fill
+// the accumulation registers, so one workgroup runs per compute unit).
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-// Output tile: 128 gathered rows (one staged chunk) x 512 columns of W; K in blocks of 32.
-constexpr int kBM = 128;
-constexpr int kBN = 512;
-constexpr int kBK = 32;
+// Output tile: 256 gathered rows (two staged chunks of one shard) x 256 columns of W;
+// K in blocks of 64 (128-byte rows, whole cache lines).
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 64;
 // Rows of a staged chunk of A: the pages' Table 3 moves AllGather+GEMM's shards in
 // chunks of 128 rows; one staging task and one ready flag per chunk.
 constexpr int kChunkRows = 128;
-static_assert(kBM == kChunkRows, "an output tile reads exactly one staged chunk");
+constexpr int kChunksPerTile = kBM / kChunkRows;
+// A chunk is staged as kPieces tasks of 64 rows, so two workgroups can copy one chunk
+// at once (the chunk's flag counts its pieces in); finer pieces cost more scheduler
+// round trips than the shorter start-up waits save.
+constexpr int kPieces = 2;
+static_assert(kChunkRows % kPieces == 0, "whole-row pieces");
+constexpr int kPieceRows = kChunkRows / kPieces;
+static_assert(kBM == 2 * kChunkRows, "an output tile reads two staged chunks");
 constexpr int kMaxXcd = 8;
 
 enum : uint32_t { kRoleCompute = 0, kRoleStage = 1 };
@@ -80,13 +89,15 @@ struct Args {
   uint16_t* c;               // [N * M_loc, N_out] bf16 (written)
   int n_ranks, rank, m_loc, k, n_out;
   int n_chunks;              // ceil(M_loc / 128): chunks per shard
-  int n_ntiles;              // ceil(N_out / 512)
+  int n_rtiles;              // ceil(M_loc / 256): row tiles per shard (two chunks each)
+  int n_ntiles;              // ceil(N_out / 256)
   int n_xcd;                 // compute queues
   int xcd_ntiles[kMaxXcd];   // column tiles of each queue (tile x, x + n_xcd, ...)
-  int n_compute;             // compute tiles in total: N * n_chunks * n_ntiles
-  int n_stage_tasks;         // N * n_chunks: every shard's chunks, the local one last
+  int n_compute;             // compute tiles in total: N * n_rtiles * n_ntiles
+  int n_stage_tasks;         // N * n_chunks * kPieces: every shard's chunks, the local one last
   // Device state (library-owned).
-  uint64_t* flags;           // [N * n_chunks]: chunk of schedule position o, index j
+  uint64_t* flags;           // [N * n_chunks]: chunk of schedule position o, index j:
+                             // (epoch << 20) | pieces staged
   Ctrl* ctrl;
   Status* status;
   uint64_t epoch;

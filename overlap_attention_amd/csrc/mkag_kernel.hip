@@ -7,7 +7,7 @@
 // GPU plays one rank: STAGING workgroups play the gather, copying every shard's
 // 128-row chunks from its home (a_shards[s], standing for rank s's memory) into the
 // gathered buffer a_full and publishing an epoch-stamped ready flag per chunk; COMPUTE
-// workgroups run C = A_full W^T in 128 x 512 output tiles, reading the local shard in
+// workgroups run C = A_full W^T in 256 x 256 output tiles (two chunks each), reading the local shard in
 // place and every other chunk from a_full once its flag is set. The staging/compute
 // split follows Eq. (2) of §3.2 (remaining tasks of each role times their measured
 // costs); a compute workgroup whose tile waits for a chunk nobody has claimed stages
@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "mkag_args.h"
 
@@ -55,8 +56,17 @@ __device__ __forceinline__ bool cas64(uint64_t* p, uint64_t expect, uint64_t des
 }
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ uint64_t stamp(uint64_t epoch) { return (epoch << 20) | 1u; }
+// A chunk's flag once all its pieces are staged in launch `epoch`.
+__device__ __forceinline__ uint64_t stamp(uint64_t epoch) { return (epoch << 20) | (uint64_t)kPieces; }
 __device__ __forceinline__ uint32_t wave_bcast(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Waits until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ bool has_error(const Args& a) { return ld32(&a.ctrl->error.v) != kErrNone; }
 __device__ __forceinline__ void raise_error(const Args& a, uint32_t code) { cas32(&a.ctrl->error.v, kErrNone, code); }
@@ -96,22 +106,26 @@ __device__ __forceinline__ bool wave_wait_stamp(const Args& a, const uint64_t* p
 
 // ------------------------------------------------------------------ staging role
 
-// Staging task s: chunk j of the shard at staging position o = s / n_chunks, rows
-// [128 j, 128 j + rows) of that shard, copied to its place in a_full; one release of
-// the chunk's epoch stamp after every thread's stores (Table 3: 128-row chunks; §4:
-// epoch-stamped readiness flags).
-__device__ __forceinline__ void stage_chunk(const Args& a, int s, bool assist) {
+// Staging task s: piece q = s % kPieces (16 rows) of chunk c = s / kPieces, which is
+// chunk j of the shard at staging position o = c / n_chunks: rows
+// [128 j + 16 q, 128 j + 16 q + 16) of that shard, copied to its place in a_full. Every
+// wave waits for its stores, then thread 0 counts the piece in on the chunk's
+// epoch-stamped flag with one agent-scope release (Table 3: 128-row chunks; §4:
+// epoch-stamped readiness flags); the chunk is ready when all kPieces are in. Pieces
+// past a ragged chunk's end copy nothing and only count in.
+__device__ __forceinline__ void stage_piece(const Args& a, int s, bool assist) {
   const int tid = threadIdx.x;
   const uint64_t t0 = ticks();
-  const int o = s / a.n_chunks, j = s % a.n_chunks;
+  const int c = s / kPieces, q = s % kPieces;
+  const int o = c / a.n_chunks, j = c % a.n_chunks;
   const int shard = staging_shard(a, o);
-  const int r0 = j * kChunkRows;
-  const int rows = min(kChunkRows, a.m_loc - r0);
+  const int r0 = j * kChunkRows + q * kPieceRows;
+  const int rows = max(0, min(kPieceRows, a.m_loc - r0));
   const int64_t off = ((int64_t)shard * a.m_loc + r0) * a.k;  // same offset in both buffers
   const u32x4* src = reinterpret_cast<const u32x4*>(a.a_shards + off);
   u32x4* dst = reinterpret_cast<u32x4*>(a.a_full + off);
-  const int64_t n16 = (int64_t)rows * a.k / 8;  // 16-byte vectors (K is a multiple of 32)
-  constexpr int kInFlight = 8;
+  const int64_t n16 = (int64_t)rows * a.k / 8;  // 16-byte vectors (K is a multiple of 64)
+  constexpr int kInFlight = 16;
   int64_t i = tid;
   for (; i + (kInFlight - 1) * kThreads < n16; i += kInFlight * kThreads) {
     u32x4 v[kInFlight];
@@ -121,11 +135,25 @@ __device__ __forceinline__ void stage_chunk(const Args& a, int s, bool assist) {
     for (int u = 0; u < kInFlight; ++u) dst[i + u * kThreads] = v[u];
   }
   for (; i < n16; i += kThreads) dst[i] = __builtin_nontemporal_load(src + i);
+  // Every wave waits for its own stores to complete (a workgroup-scope fence alone does
+  // not: it emits no wait before the barrier); thread 0's agent-scope release then
+  // covers the whole piece.
+  wait_vm<0>();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0) {
     fence_release();
-    __hip_atomic_store(&a.flags[s], stamp(a.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Count in: a flag stamped by an earlier launch counts as zero pieces.
+    uint64_t* f = &a.flags[c];
+    uint64_t v = ld64(f);
+    while (true) {
+      const uint64_t before = (v >> 20) == a.epoch ? (v & 0xfffffull) : 0;
+      uint64_t expect = v;
+      if (__hip_atomic_compare_exchange_strong(f, &expect, (a.epoch << 20) | (before + 1), __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        break;
+      v = expect;
+    }
     add64(&a.ctrl->stage_ticks.v, ticks() - t0);
     add32(&a.ctrl->stage_done.v, 1);
     if (assist) add32(&a.ctrl->assist_tasks.v, 1);
@@ -134,130 +162,226 @@ __device__ __forceinline__ void stage_chunk(const Args& a, int s, bool assist) {
 
 // ------------------------------------------------------------------ compute role
 
-// LDS: two stages, each an A tile (128 rows x 32 k) and a W tile (512 rows x 32 k),
-// rows of 64 bytes whose four 16-byte chunks are swizzled (chunk c of row r at
-// c ^ ((r >> 1) & 3)) so the MFMA operand reads of a wave are bank-conflict free.
-constexpr int kRowBytes = kBK * 2;
-constexpr int kATileBytes = kBM * kRowBytes;  // 8 KB
-constexpr int kWTileBytes = kBN * kRowBytes;  // 32 KB
-constexpr int kStageBytes = kATileBytes + kWTileBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;
-__shared__ __attribute__((aligned(16))) uint8_t g_lds[kLdsBytes];
+// LDS: two stages, each an A tile (256 rows x 64 k, 32 KB) and a W tile (256 rows x
+// 64 k, 32 KB) in rows of 128 bytes whose eight 16-byte chunks are swizzled (chunk c
+// of row r sits at c ^ ((r >> 1) & 7)): any 16 consecutive lanes of an operand read
+// (rows r0..r0+15, one chunk index) then cover all 64 banks once.
+constexpr int kStages = 2;
+constexpr int kRowBytes = kBK * 2;                      // 128
+constexpr int kATileBytes = kBM * kRowBytes;            // 32 KB
+constexpr int kWTileBytes = kBN * kRowBytes;            // 32 KB
+constexpr int kStageBytes = kATileBytes + kWTileBytes;  // 64 KB
+constexpr int kLdsBytes = kStages * kStageBytes;        // 128 KB
+// A stage is filled by 1 KB block copies (global_load_lds_dwordx4: 64 lanes x 16
+// bytes straight into LDS, no registers), 8 rows of 128 bytes each, so every copy
+// reads 8 whole cache lines. Copy i of wave w fills block w + kWaves i: blocks 0..31
+// hold A rows, 32..63 W rows.
+constexpr int kRowsPerCopy = 1024 / kRowBytes;         // 8
+constexpr int kCopies = kStageBytes / 1024 / kWaves;   // 16 per wave per stage
+constexpr int kCopiesA = kATileBytes / 1024 / kWaves;  // the first 8 of them A
+constexpr int kCopiesPerSlice = kCopies / 2;           // issued over one k-slice's MFMAs
+static_assert(kStageBytes % (1024 * kWaves) == 0 && kATileBytes % (1024 * kWaves) == 0, "whole copies");
+__shared__ __attribute__((aligned(1024))) uint8_t g_lds[kLdsBytes];
 __shared__ int32_t g_cmd[4];
 
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 3); }
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint32_t lds_base() { return (uint32_t)(uintptr_t)((lds_void*)g_lds); }
 
-// One output tile: gathered chunk ci (compute order) x column tile nt.
-__device__ __forceinline__ void compute_tile(const Args& a, int ci, int nt, uint64_t& waited) {
+// A 64-bit pointer that is the same in every lane, moved to SGPRs.
+__device__ __forceinline__ const uint16_t* wave_bcast_ptr(const uint16_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  return (const uint16_t*)(uintptr_t)(((uint64_t)wave_bcast((uint32_t)(v >> 32)) << 32) | wave_bcast((uint32_t)v));
+}
+
+// Workgroup barrier that also orders this wave's LDS reads before it: the copies
+// issued after it overwrite a stage the reads came from. The empty asm statements keep
+// the compiler from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy i of this wave for the K block whose tile rows start at a_src / w_src
+// (wave-uniform), into the stage at LDS address m0s (+ this wave's block).
+template <int I>
+__device__ __forceinline__ void copy_one(const uint32_t (&voff)[kCopies], const uint16_t* a_src,
+                                         const uint16_t* w_src, uint32_t m0s) {
+  const uint32_t m0 = m0s + (uint32_t)(I * kWaves * 1024);
+  if constexpr (I < kCopiesA)
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff[I]), "s"(a_src), "{m0}"(m0) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff[I]), "s"(w_src), "{m0}"(m0) : "memory");
+}
+
+template <int... I>
+__device__ __forceinline__ void copy_all(std::integer_sequence<int, I...>, const uint32_t (&voff)[kCopies],
+                                         const uint16_t* a_src, const uint16_t* w_src, uint32_t m0s) {
+  (copy_one<I>(voff, a_src, w_src, m0s), ...);
+}
+
+// Operand f of a 16-wide k-slice: f < 4 the wave's W rows 32 f + (lane % 32) of its
+// 128, f >= 4 its A rows 32 (f - 4) + (lane % 32); each lane's 8 k values of chunk
+// 2 kk + lane / 32 (w_off / a_off carry the wave's rows, kk and the lane's swizzled
+// position).
+__device__ __forceinline__ bf16x8 read_operand(const uint8_t* sb, int w_off, int a_off, int f) {
+  return *reinterpret_cast<const bf16x8*>(sb + (f < 4 ? w_off + 4096 * f : a_off + 4096 * (f - 4)));
+}
+
+// The 16 MFMAs of one k-slice on operands f, product q = (A block m = q / 4, W block
+// t = q % 4), so consecutive MFMAs share their B operand. After MFMA q: operand q of
+// the next slice is read into g (q < 8, READ), and with COPY >= 0 copy COPY + q / 2 is
+// issued after every other MFMA, so no wave issues several copies at once and waits for
+// the memory pipeline to take them while its matrix core idles. The order is fixed
+// (sched_barrier): the compiler may not gather the reads or copies into one burst.
+template <bool READ, int COPY>
+__device__ __forceinline__ void slice(f32x16 (&acc)[4][4], const bf16x8 (&f)[8], bf16x8 (&g)[8], const uint8_t* gsb,
+                                      int w_off, int a_off, const uint32_t (&voff)[kCopies], const uint16_t* a_src,
+                                      const uint16_t* w_src, uint32_t m0s) {
+  static_assert(COPY < 0 || COPY + kCopiesPerSlice <= kCopies, "copy range");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int m = q >> 2, t = q & 3;
+    acc[t][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[t], f[4 + m], acc[t][m], 0, 0, 0);
+    if (READ && q < 8) g[q] = read_operand(gsb, w_off, a_off, q);
+    if constexpr (COPY >= 0) {
+      if (q % 2 == 0) {
+        // q / 2 is a constant after unrolling; dispatch it to the template.
+        switch (q / 2) {
+          case 0: copy_one<COPY + 0>(voff, a_src, w_src, m0s); break;
+          case 1: copy_one<COPY + 1>(voff, a_src, w_src, m0s); break;
+          case 2: copy_one<COPY + 2>(voff, a_src, w_src, m0s); break;
+          case 3: copy_one<COPY + 3>(voff, a_src, w_src, m0s); break;
+          case 4: copy_one<COPY + 4>(voff, a_src, w_src, m0s); break;
+          case 5: copy_one<COPY + 5>(voff, a_src, w_src, m0s); break;
+          case 6: copy_one<COPY + 6>(voff, a_src, w_src, m0s); break;
+          default: copy_one<COPY + 7>(voff, a_src, w_src, m0s); break;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Bounded wait for the ready flag of chunk f (staging order).
+__device__ __forceinline__ bool wait_chunk(const Args& a, int f, uint64_t& waited) {
+  return wave_wait_stamp(a, &a.flags[f], stamp(a.epoch), waited);
+}
+
+// One output tile: row tile rt (compute order) x column tile nt. K blocks of 64 flow
+// through the two LDS stages. Block kb + 1 is copied while block kb is consumed: its
+// first half once every wave has read block kb - 1 (during the last k-slice of block
+// kb - 1), its second half during the first k-slice of block kb; one barrier per block,
+// before its last k-slice, after which the next block's first operands are read.
+__device__ __forceinline__ void compute_tile(const Args& a, int rt, int nt, uint64_t& waited) {
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int w = (int)wave_bcast((uint32_t)(tid >> 6));
-  const int wm = w >> 2, wn = w & 3;  // wave block: rows wm*64.., columns wn*128..
-  ci = (int)wave_bcast((uint32_t)ci);
+  const int wm = w >> 1, wn = w & 1;  // wave block: rows wm*128.., columns wn*128..
+  rt = (int)wave_bcast((uint32_t)rt);
   nt = (int)wave_bcast((uint32_t)nt);
-  const int p = ci / a.n_chunks, j = ci % a.n_chunks;
+  const int p = rt / a.n_rtiles, jj = rt % a.n_rtiles;
   const int shard = compute_shard(a, p);
-  const int r0 = j * kChunkRows;
+  const int r0 = jj * kBM;
   const int rows = min(kBM, a.m_loc - r0);
   const int n0 = nt * kBN;
   const int cols = min(kBN, a.n_out - n0);
   const int64_t grow0 = (int64_t)shard * a.m_loc + r0;  // first gathered row of the tile
   // The local shard is read in place; every other chunk from a_full once staged.
-  const uint16_t* asrc = (p == 0 ? a.a_shards : a.a_full) + grow0 * a.k;
+  const uint16_t* asrc = wave_bcast_ptr((p == 0 ? a.a_shards : a.a_full) + grow0 * a.k);
+  const uint16_t* wsrc = wave_bcast_ptr(a.w + (int64_t)n0 * a.k);
   bool ok = true;
-  if (p > 0) ok = wave_wait_stamp(a, &a.flags[ci - a.n_chunks], stamp(a.epoch), waited);
-
-  // Loads of one K block: thread t moves 16-byte chunk (t & 3) of A row t >> 2 and of W
-  // rows (t >> 2) + 128 u, u = 0..3. Rows past the tile's end read a valid row (their
-  // results are never stored).
-  const int lr = tid >> 2, lc = tid & 3;
-  const uint16_t* a_row = asrc + (int64_t)min(lr, rows - 1) * a.k + lc * 8;
-  const uint16_t* w_row[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) w_row[u] = a.w + (int64_t)(n0 + min(lr + 128 * u, cols - 1)) * a.k + lc * 8;
-  const int a_st = lr * kRowBytes + 16 * swz(lr, lc);
-  int w_st[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) w_st[u] = kATileBytes + (lr + 128 * u) * kRowBytes + 16 * swz(lr + 128 * u, lc);
-  u32x4 ra, rw[4];
-  auto load = [&](int kb) __attribute__((always_inline)) {
-    const int k0 = kb * kBK;
-    ra = *reinterpret_cast<const u32x4*>(a_row + k0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rw[u] = *reinterpret_cast<const u32x4*>(w_row[u] + k0);
-  };
-  auto store = [&](int stage) __attribute__((always_inline)) {
-    uint8_t* base = g_lds + stage * kStageBytes;
-    *reinterpret_cast<u32x4*>(base + a_st) = ra;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(base + w_st[u]) = rw[u];
-  };
-
-  // Operand reads: W rows wn*128 + 32 t + col (t = 0..3) and A rows wm*64 + 32 m + col
-  // (m = 0..1), 16-byte chunk 2 kk + hi of the 64-byte row for k-slice kk.
-  int w_rd[4][2], a_rd[2][2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = wn * 128 + 32 * t + col;
-      w_rd[t][kk] = kATileBytes + r * kRowBytes + 16 * swz(r, 2 * kk + hi);
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = wm * 64 + 32 * m + col;
-      a_rd[m][kk] = r * kRowBytes + 16 * swz(r, 2 * kk + hi);
-    }
+  if (p > 0) {
+    // Flag of chunk j of the shard at compute position p >= 1: (p - 1) n_chunks + j.
+    const int f0 = (p - 1) * a.n_chunks + kChunksPerTile * jj;
+    ok = wait_chunk(a, f0, waited);
+    if (ok && kChunksPerTile * jj + 1 < a.n_chunks) ok = wait_chunk(a, f0 + 1, waited);
   }
-  f32x16 acc[4][2];
+  wait_vm<0>();  // older loads and stores of this wave: the counts below cover copies only
+
+  // Copy lanes: lane l fills LDS chunk l % 8 of row l / 8 of its 1 KB block, which holds
+  // k-chunk (l % 8) ^ ((row >> 1) & 7) of that row. Rows past the tile's end read a
+  // valid row (their results are never stored).
+  const uint32_t row_bytes = (uint32_t)a.k * 2u;
+  uint32_t voff[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int b = w + kWaves * i;
+    const int r = (i < kCopiesA ? b : b - kBM / kRowsPerCopy) * kRowsPerCopy + (lane >> 3);
+    const int rc = i < kCopiesA ? min(r, rows - 1) : min(r, cols - 1);
+    voff[i] = (uint32_t)rc * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+  }
+  const uint32_t m0w = wave_bcast(lds_base() + (uint32_t)w * 1024u);
+
+  // Operand reads: row r = 32 x + col of a 32-row group, chunk 2 kk + hi, swizzled by
+  // (r >> 1) & 7 = (col >> 1) & 7.
+  int a_off[4], w_off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int lo = col * kRowBytes + 16 * ((2 * kk + hi) ^ ((col >> 1) & 7));
+    a_off[kk] = wm * 128 * kRowBytes + lo;
+    w_off[kk] = kATileBytes + wn * 128 * kRowBytes + lo;
+  }
+  f32x16 acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) acc[t][m] = f32x16{};
+    for (int m = 0; m < 4; ++m) acc[t][m] = f32x16{};
 
+  // Every iteration has the same shape (branches here would split the accumulators'
+  // registers): copies past the last block re-read the last block into the stage that
+  // is not read again, and the last iteration's reads of the next block's first slice
+  // are of valid LDS.
   const int nk = a.k / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
+  const auto blk = [&](int x) { return min(x, nk - 1) * kBK; };
+  copy_all(std::make_integer_sequence<int, kCopies>{}, voff, asrc, wsrc, m0w);
+  copy_all(std::make_integer_sequence<int, kCopiesPerSlice>{}, voff, asrc + blk(1), wsrc + blk(1),
+           m0w + (uint32_t)kStageBytes);
+  wait_vm<kCopiesPerSlice>();  // block 0
+  stage_barrier();
+  bf16x8 cur[8], nxt[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) cur[f] = read_operand(g_lds, w_off[0], a_off[0], f);
   for (int kb = 0; kb < nk; ++kb) {
-    const int stage = kb & 1;
-    if (kb + 1 < nk) load(kb + 1);  // in flight during the MFMAs below
-    const uint8_t* base = g_lds + stage * kStageBytes;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 wf[4], af[2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) wf[t] = *reinterpret_cast<const bf16x8*>(base + w_rd[t][kk]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) af[m] = *reinterpret_cast<const bf16x8*>(base + a_rd[m][kk]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) acc[t][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], af[m], acc[t][m], 0, 0, 0);
-    }
-    if (kb + 1 < nk) store(stage ^ 1);  // the stage read one block ago, freed by the barrier below
-    __syncthreads();
+    const int s = kb & 1;
+    const uint8_t* sb = g_lds + s * kStageBytes;
+    const uint8_t* sb1 = g_lds + (s ^ 1) * kStageBytes;
+    const uint32_t m0s = m0w + (uint32_t)(s * kStageBytes), m0s1 = m0w + (uint32_t)((s ^ 1) * kStageBytes);
+    const int x1 = blk(kb + 1), x2 = blk(kb + 2);
+    // Slice 0 (second half of block kb + 1's copies), slices 1 and 2.
+    slice<true, kCopiesPerSlice>(acc, cur, nxt, sb, w_off[1], a_off[1], voff, asrc + x1, wsrc + x1, m0s1);
+    slice<true, -1>(acc, nxt, cur, sb, w_off[2], a_off[2], voff, nullptr, nullptr, 0);
+    slice<true, -1>(acc, cur, nxt, sb, w_off[3], a_off[3], voff, nullptr, nullptr, 0);
+    // Block kb + 1 has landed (this wave's copies; the barrier covers the others') and
+    // every wave has read stage s: it takes block kb + 2's first half during slice 3,
+    // while block kb + 1's first slice is read.
+    wait_vm<0>();
+    stage_barrier();
+    slice<true, 0>(acc, nxt, cur, sb1, w_off[0], a_off[0], voff, asrc + x2, wsrc + x2, m0s);
   }
+  wait_vm<0>();  // the copies past the end, before the next tile fills the stages
 
-  // acc[t][m] element i: output row wm*64 + 32 m + col, column wn*128 + 32 t + 8 (i/4) +
-  // 4 hi + (i % 4); four consecutive columns go out as one 8-byte store.
+  // acc[t][m] element i: output row wm*128 + 32 m + col, column wn*128 + 32 t + 8 (i/4)
+  // + 4 hi + (i % 4); four consecutive columns go out as one 8-byte store.
   if (ok) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = wm * 64 + 32 * m + col;
-      if (r >= rows) continue;
+    for (int m = 0; m < 4; ++m) {
+      const int r = wm * 128 + 32 * m + col;
       uint16_t* crow = a.c + (grow0 + r) * a.n_out + n0;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int cc = wn * 128 + 32 * t + 8 * g + 4 * hi;
-          if (cc >= cols) continue;  // N_out is a multiple of 8: a group is whole or absent
-          bf16x4 v;
-          v[0] = (__bf16)acc[t][m][4 * g + 0];
-          v[1] = (__bf16)acc[t][m][4 * g + 1];
-          v[2] = (__bf16)acc[t][m][4 * g + 2];
-          v[3] = (__bf16)acc[t][m][4 * g + 3];
-          *reinterpret_cast<bf16x4*>(crow + cc) = v;
+          // N_out is a multiple of 8: a group of four columns is whole or absent.
+          if (r < rows && cc < cols) {
+            bf16x4 b;
+            b[0] = (__bf16)acc[t][m][4 * g + 0];
+            b[1] = (__bf16)acc[t][m][4 * g + 1];
+            b[2] = (__bf16)acc[t][m][4 * g + 2];
+            b[3] = (__bf16)acc[t][m][4 * g + 3];
+            *reinterpret_cast<bf16x4*>(crow + cc) = b;
+          }
         }
     }
   }
@@ -279,14 +403,15 @@ __device__ __forceinline__ int eq2_target(int64_t b, int64_t rp, int64_t rs, int
 
 __device__ __forceinline__ int target_of(const Args& a, uint32_t v) { return v == 0 ? a.initial_stagers : (int)v - 1; }
 
+// Queue x: its column tiles of every row tile, in compute order.
 __device__ __forceinline__ int64_t queue_len(const Args& a, int x) {
-  return (int64_t)a.n_ranks * a.n_chunks * a.xcd_ntiles[x];
+  return (int64_t)a.n_ranks * a.n_rtiles * a.xcd_ntiles[x];
 }
 
 struct Sched {
   int32_t role;
   int32_t pending;
-  int32_t pend_ci, pend_nt;
+  int32_t pend_rt, pend_nt;
 };
 
 // Run by lane 0 of wave 0: picks the workgroup's next task and writes (op, x, y).
@@ -317,7 +442,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
       } else {
         // Measured ticks averaged with the cost model's priors, weighted as one shard's
         // tasks of each role, so the first (cold) tasks do not swing the split.
-        const uint64_t kc = (uint64_t)a.n_chunks * a.n_ntiles, ks = (uint64_t)a.n_chunks;
+        const uint64_t kc = (uint64_t)a.n_rtiles * a.n_ntiles, ks = (uint64_t)a.n_chunks;
         cp = (int64_t)((ld64(&a.ctrl->compute_ticks.v) + kc * (uint64_t)a.cost_compute0) / (cd + kc));
         cs = (int64_t)((ld64(&a.ctrl->stage_ticks.v) + ks * (uint64_t)a.cost_stage0) / (sd + ks));
       }
@@ -364,7 +489,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
       const uint32_t h = add32(&a.ctrl->xcd_head[q].v, 1);
       if ((int64_t)h >= len) continue;
       const int nq = a.xcd_ntiles[q];
-      st->pend_ci = (int32_t)(h / nq);
+      st->pend_rt = (int32_t)(h / nq);
       st->pend_nt = q + a.n_xcd * (int32_t)(h % nq);
       st->pending = 1;
     }
@@ -383,14 +508,17 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
       return;
     }
   }
-  // The stall rule of §3.2: while the chunk the claimed tile reads is unclaimed
-  // staging, stage first (claiming the staging head up to that chunk). A failed
+  // The stall rule of §3.2: while a chunk the claimed tile reads is unclaimed staging,
+  // stage first (claiming the staging head up to the last piece of the tile's later
+  // chunk). A failed
   // compare-and-swap returns a larger head, so the loop ends within need - head + 1
-  // attempts, either with a claim or with the chunk claimed by someone else (who is
-  // staging it: the tile's wait on its flag then ends).
-  const int p = st->pend_ci / a.n_chunks;
+  // attempts, either with a claim or with the chunks claimed by others (who are
+  // staging them: the tile's waits on their flags then end).
+  const int p = st->pend_rt / a.n_rtiles;
   if (p > 0) {
-    const int need = st->pend_ci - a.n_chunks;  // staging task of the tile's chunk
+    const int jj = st->pend_rt % a.n_rtiles;
+    const int need =
+        ((p - 1) * a.n_chunks + min(kChunksPerTile * jj + kChunksPerTile - 1, a.n_chunks - 1)) * kPieces + kPieces - 1;
     uint32_t h = ld32(&a.ctrl->stage_head.v);
     while ((int)h <= need) {
       uint32_t expect = h;
@@ -405,7 +533,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
     }
   }
   op = kOpCompute;
-  x = st->pend_ci;
+  x = st->pend_rt;
   y = st->pend_nt;
   st->pending = 0;
   cmd[0] = op;
@@ -434,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void ag_gemm_kernel(Args a) {
     const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
     if (op == kOpExit) break;
     if (op == kOpStage) {
-      stage_chunk(a, x, y != 0);
+      stage_piece(a, x, y != 0);
     } else {
       const uint64_t t0 = ticks();
       uint64_t waited = 0;

@@ -47,7 +47,7 @@ def test_invalid_arguments_rejected_on_host(name):
     assert mk.load_library().mk_last_error().decode() != ""
 
 
-@pytest.mark.parametrize("k,no", [(48, 1024), (512, 1020)])
+@pytest.mark.parametrize("k,no", [(48, 1024), (96, 1024), (512, 1020)])
 def test_unsupported_shapes(k, no):
     a, w, f, c = good(k=k, no=no)
     assert call(a, 4, 1, w, f, c) == mk.MK_E_UNSUPPORTED

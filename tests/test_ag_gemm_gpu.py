@@ -56,8 +56,8 @@ def check(cfg, seed, rows=None, **kw):
 
 SHAPES = [
     AG_CONFIGS[0],
-    AgConfig("ragged_r2of3_M200_K96_N520", n_ranks=3, rank=2, m_loc=200, k=96, n_out=520),
-    AgConfig("one_row_r0of5_K32_N8", n_ranks=5, rank=0, m_loc=1, k=32, n_out=8),
+    AgConfig("ragged_r2of3_M200_K192_N520", n_ranks=3, rank=2, m_loc=200, k=192, n_out=520),
+    AgConfig("one_row_r0of5_K64_N8", n_ranks=5, rank=0, m_loc=1, k=64, n_out=8),
     AgConfig("single_rank_M300_K64_N1024", n_ranks=1, rank=0, m_loc=300, k=64, n_out=1024),
     AgConfig("two_chunks_r1of2_M130_K128_N1536", n_ranks=2, rank=1, m_loc=130, k=128, n_out=1536),
     AgConfig("many_ranks_r9of16_M64_K256_N512", n_ranks=16, rank=9, m_loc=64, k=256, n_out=512),
@@ -118,8 +118,8 @@ def test_stats_count_every_task():
     _, _, st = run_gpu(cfg, a.cuda(), w.cuda(), want_stats=True)
     print("    stats:", st, flush=True)
     assert st["status"] == 0
-    assert st["compute_done"] == st["compute_tiles"] == 8 * 2 * 2
-    assert st["staging_done"] == st["staging_tasks"] == 8 * 2
+    assert st["compute_done"] == st["compute_tiles"] == 8 * 1 * 4  # ranks x 256-row tiles x 256-column tiles
+    assert st["staging_done"] == st["staging_tasks"] == 8 * 2 * 2  # ranks x chunks x 64-row pieces
 
 
 @pytest.mark.timeout(600)
