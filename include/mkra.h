@@ -117,7 +117,18 @@ typedef struct {
                                   none), < 0 = none. */
   int32_t tail_steps_per_task; /* 1..steps_per_task (larger values are clamped to it);
                                   0 = default (2). */
-  int32_t reserved[2];
+  int32_t parallel_steps;      /* 1: a unit's step groups run at once, each from a fresh
+                                  online-softmax state, and the group that finishes last
+                                  merges the partial (O, m, l) in group order (the
+                                  mathematics of the per-chunk LSE merge, in fp32);
+                                  -1: never (a unit's groups run in order, the state
+                                  carried); 0 = default: on when the units fill at most
+                                  half of the device's workgroup slots. With it,
+                                  steps_per_task defaults to a quarter of the steps,
+                                  clamped to 2..4, and there is no default tail.
+                                  Results are reproducible for a given mode and
+                                  grouping (the merge runs in group order). */
+  int32_t reserved;
 } mk_ring_attn_opts;
 
 /* Filled by mk_ring_attn_fwd_ex when stats != NULL (the call then synchronises the
@@ -154,6 +165,9 @@ typedef struct {
   int32_t steps_per_task;      /* ring steps per compute task in this launch (before
                                   the tail) */
   int32_t step_groups;         /* compute tasks per unit */
+  int32_t parallel_steps;      /* 1 if the launch ran its step groups at once (see
+                                  mk_ring_attn_opts.parallel_steps) */
+  int32_t reserved;
 } mk_ring_attn_stats;
 
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,

@@ -46,7 +46,8 @@ class mk_ring_attn_opts(ctypes.Structure):
         ("steps_per_task", ctypes.c_int32),
         ("tail_steps", ctypes.c_int32),
         ("tail_steps_per_task", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("parallel_steps", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -77,6 +78,8 @@ class mk_ring_attn_stats(ctypes.Structure):
         ("wg_ticks", ctypes.c_int64),
         ("steps_per_task", ctypes.c_int32),
         ("step_groups", ctypes.c_int32),
+        ("parallel_steps", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self):

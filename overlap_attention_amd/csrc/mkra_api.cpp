@@ -378,6 +378,8 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     return fail(MK_E_INVAL, "opts.steps_per_task must be 0 (default) or 1..4");
   if (opts.tail_steps_per_task < 0 || opts.tail_steps_per_task > mkra::kMaxGroup)
     return fail(MK_E_INVAL, "opts.tail_steps_per_task must be 0 (default) or 1..4");
+  if (opts.parallel_steps < -1 || opts.parallel_steps > 1)
+    return fail(MK_E_INVAL, "opts.parallel_steps must be -1, 0 or 1");
   if (opts.fixed_staging_wgs < 0 || opts.initial_staging_wgs < 0 || opts.grid_wgs < 0 || opts.spin_timeout_us < 0 ||
       opts.controller_period_us < 0 || opts.trace_capacity < 0 || opts.stage_delay_ticks < 0)
     return fail(MK_E_INVAL, "negative option");
@@ -436,27 +438,49 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   if ((s = device_info(dev, &di)) != MK_OK) return s;
   const int capacity = di->cus * di->occ[d == 128 ? 1 : 0];
   int grid = opts.grid_wgs > 0 ? std::min(opts.grid_wgs, capacity) : capacity;
-  // No more workgroups than tasks can use at once.
-  const int64_t useful = n_units + std::min<int64_t>(n_stage_tasks, 16);
-  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, useful));
-  a.grid = grid;
-  a.n_xcd = std::min(mkra::kMaxXcd, grid);
-  for (int x = 0; x <= a.n_xcd; ++x) a.xcd_unit_begin[x] = (int)((int64_t)x * n_units / a.n_xcd);
+  // Parallel step groups: by default when the units fill at most half of the device's
+  // workgroup slots, so that a unit's ring steps, run at once and merged, spread the
+  // work (the unfused baseline runs one step per launch and keeps the carried state).
+  // The choice and the group size depend on the device, not on opts.grid_wgs, so a
+  // smaller grid gives the same result bits.
+  a.parallel_steps =
+      n_steps > 1 && copy_stream == nullptr &&
+              (opts.parallel_steps > 0 || (opts.parallel_steps == 0 && n_units * 2 <= (int64_t)capacity))
+          ? 1
+          : 0;
 
   // Step groups: `group` steps each, except the last tail_steps steps, which run in
-  // groups of tail_group (shorter tasks at the end shorten the launch's tail).
-  a.group = opts.steps_per_task > 0 ? opts.steps_per_task : default_steps_per_task(lk, d);
+  // groups of tail_group (shorter tasks at the end shorten the launch's tail). With
+  // parallel groups the default is a quarter of the steps, 2..4: a task's fixed costs
+  // (flags, pipeline fill, the partial's store and merge) weigh about as much as one
+  // step of a small problem, so one-step tasks lose to longer ones (measured on the
+  // 8K-token and 6K-24K-token workloads).
+  const int parallel_group = std::max(2, std::min(mkra::kMaxGroup, n_steps / 4));
+  a.group = opts.steps_per_task > 0 ? opts.steps_per_task
+            : a.parallel_steps      ? parallel_group
+                                    : default_steps_per_task(lk, d);
   a.tail_group = opts.tail_steps_per_task > 0 ? std::min(opts.tail_steps_per_task, a.group)
                                               : std::min(kDefaultTailStepsPerTask, a.group);
   {
-    // By default only a launch whose units outnumber its workgroups (several rounds of
-    // tasks) has a tail; with fewer units every task starts at once.
-    const int tail_default = (a.group > kDefaultTailStepsPerTask && n_units > (int64_t)a.grid) ? kDefaultTailSteps : 0;
+    // By default only a sequential launch whose units outnumber its workgroups (several
+    // rounds of tasks) has a tail; with fewer units every task starts at once. Parallel
+    // groups take no default tail: their grouping sets the merge, and it must not
+    // depend on the grid.
+    const int tail_default =
+        (!a.parallel_steps && a.group > kDefaultTailStepsPerTask && n_units > (int64_t)grid) ? kDefaultTailSteps : 0;
     const int tail_steps = opts.tail_steps > 0 ? opts.tail_steps : opts.tail_steps < 0 ? 0 : tail_default;
     a.n_big = std::max(0, n_steps - tail_steps) / a.group;
     const int rest = n_steps - a.n_big * a.group;
     a.n_groups = a.n_big + (rest + a.tail_group - 1) / a.tail_group;
   }
+  // No more workgroups than tasks can use at once.
+  const int64_t useful = n_units * (a.parallel_steps ? (int64_t)a.n_groups : 1) + std::min<int64_t>(n_stage_tasks, 16);
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, useful));
+  a.grid = grid;
+  a.n_xcd = std::min(mkra::kMaxXcd, grid);
+  for (int x = 0; x <= a.n_xcd; ++x) a.xcd_unit_begin[x] = (int)((int64_t)x * n_units / a.n_xcd);
+  // Running-state slots: one per unit, or one per (unit, step group) with parallel groups.
+  const int64_t state_slots = n_units * (a.parallel_steps ? (int64_t)a.n_groups : 1);
 
   // Cost model for the controller's priors and the initial split (Eq. (2) with
   // modelled costs; §3.2: the data dependency sets the initial allocation).
@@ -502,7 +526,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     const uint64_t o_slots = o_uflags + align256((uint64_t)n_units * sizeof(uint64_t));
     const uint64_t o_acc = o_slots + align256((uint64_t)mkra::kSlots * a.slot_bytes + mkra::kDiscardBytes);
     const uint64_t need =
-        o_acc + (n_steps > 1 ? (uint64_t)n_units * mkra::kWaves * (32 * d + 256) * sizeof(float) : 0);
+        o_acc + (n_steps > 1 ? (uint64_t)state_slots * mkra::kWaves * (32 * d + 256) * sizeof(float) : 0);
     if (need > mkra::kScratchBytes)
       return fail(MK_E_UNSUPPORTED, "this problem needs " + std::to_string(need) +
                                         " bytes of device state; the no-allocation entry point holds " +
@@ -553,7 +577,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   // The ring slots, then one block of scratch that the compute role's discarded copies
   // read (its contents are never used).
   GROW(slots, w->slot_bytes_cap, mkra::kSlots * (size_t)a.slot_bytes + mkra::kDiscardBytes, false);
-  if (n_steps > 1) GROW(acc, w->acc_cap, (size_t)n_units * mkra::kWaves * (32 * d + 256), false);
+  if (n_steps > 1) GROW(acc, w->acc_cap, (size_t)state_slots * mkra::kWaves * (32 * d + 256), false);
   if (opts.trace) {
     size_t cap = (size_t)(opts.trace_capacity > 0 ? opts.trace_capacity : 262144);
     size_t tc = (size_t)w->trace_cap;
@@ -626,6 +650,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     stats->wg_ticks = ds.wg_ticks;
     stats->steps_per_task = a.group;
     stats->step_groups = a.n_groups;
+    stats->parallel_steps = a.parallel_steps;
   }
   return MK_OK;
 }

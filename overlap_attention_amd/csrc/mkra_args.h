@@ -141,6 +141,9 @@ struct KernelArgs {
   int n_big;              // step groups of `group` steps
   int tail_group;         // ring steps of each later step group, 1..group
   int n_groups;           // step groups: compute tasks per unit in this launch
+  int parallel_steps;     // 1: a unit's step groups run independently from a fresh state,
+                          // each storing its partial (O, m, l) in its own state slot; the
+                          // group that finishes last merges them in group order
   int step_lo;            // first ring step of this launch's step groups (0 when fused)
   int stage_lo;           // first staging task of this launch (0 when fused)
   int external_order;     // 1: launches ordered by stream events (the unfused two-stream

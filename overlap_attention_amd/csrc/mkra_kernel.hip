@@ -738,6 +738,33 @@ __device__ __forceinline__ void task_tile_flag(const KernelArgs& a, int t_first,
   want = stamp(a.epoch, t);
 }
 
+// Finalise a wave's rows: out = O / l, lse = ln(2) * (m + log2 l), with l summed over
+// the two lanes that hold a row's halves.
+template <int D>
+__device__ __forceinline__ void finalize_rows(const KernelArgs& a, const f32x16 (&o)[D / 32], float m_run,
+                                              float l_run, int qrow, int h, int hi) {
+  constexpr int DB = D / 32;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow < a.lq) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = a.out + ((int64_t)qrow * a.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+        v[0] = (__bf16)(o[db][g * 4 + 0] * inv);
+        v[1] = (__bf16)(o[db][g * 4 + 1] * inv);
+        v[2] = (__bf16)(o[db][g * 4 + 2] * inv);
+        v[3] = (__bf16)(o[db][g * 4 + 3] * inv);
+        *reinterpret_cast<bf16x4*>(op + db * 32 + g * 8 + hi * 4) = v;
+      }
+    if (hi == 0) a.lse[(int64_t)h * a.lq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+__shared__ uint32_t g_merge;  // parallel step groups: this workgroup's task merges its unit
+
 // claim_next() picks the workgroup's next task (wave 1); it runs alongside the publish.
 template <int D, class ClaimNext>
 __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
@@ -784,7 +811,10 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   // of P.
   f32x16 o[DB];
   float m_run, l_run;
-  float* accw = a.acc + ((int64_t)unit * kWaves + w) * (32 * D + 256);
+  // State slot: the unit's (carried from group to group), or with parallel step groups
+  // this group's own partial.
+  const int64_t slot_of_state = a.parallel_steps ? (int64_t)unit * a.n_groups + step_group : (int64_t)unit;
+  float* accw = a.acc + (slot_of_state * kWaves + w) * (32 * D + 256);
   // Per-lane LDS addresses (the swizzles depend only on the lane).
   LaneAddr<D> la;
   {
@@ -850,7 +880,7 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
     if (lane < 63 && lane < n_task_tiles) {
       task_tile_flag(a, t_first, nt0, ntf, lane, f, want);
       r0 = ld64(f) == want;
-    } else if (lane == 63 && t_first > 0) {
+    } else if (lane == 63 && t_first > 0 && !a.parallel_steps) {
       r0 = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t_first - 1);
     }
     if (63 + lane < n_task_tiles) {
@@ -870,7 +900,7 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
     }
   }
 
-  if (t_first == 0) {
+  if (t_first == 0 || a.parallel_steps) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     m_run = -INFINITY;
@@ -1175,25 +1205,8 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
 
 
   if (ok && wave_rows) {
-    if (t_end == a.n_steps) {
-      // Finalise: out = O / l, lse = ln(2) * (m + log2 l).
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
-      if (qrow < a.lq) {
-        const float inv = 1.f / l_tot;
-        uint16_t* op = a.out + ((int64_t)qrow * a.hq + h) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 v;
-            v[0] = (__bf16)(o[db][g * 4 + 0] * inv);
-            v[1] = (__bf16)(o[db][g * 4 + 1] * inv);
-            v[2] = (__bf16)(o[db][g * 4 + 2] * inv);
-            v[3] = (__bf16)(o[db][g * 4 + 3] * inv);
-            *reinterpret_cast<bf16x4*>(op + db * 32 + g * 8 + hi * 4) = v;
-          }
-        if (hi == 0) a.lse[(int64_t)h * a.lq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
+    if (t_end == a.n_steps && !a.parallel_steps) {
+      finalize_rows<D>(a, o, m_run, l_run, qrow, h, hi);
     } else {
       f32x4* a4 = reinterpret_cast<f32x4*>(accw);
 #pragma unroll
@@ -1226,9 +1239,58 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   }
   if (tid == 0 && ok) {
     fence_release();
-    __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t_end - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.parallel_steps) {
+      // Count this group in on the unit's epoch-stamped counter (a stamp of an earlier
+      // launch counts as zero); the last group in merges.
+      uint64_t* f = &a.unit_flags[unit];
+      uint64_t v = ld64(f), before;
+      while (true) {
+        before = (v >> 20) == a.epoch ? (v & 0xfffffull) : 0;
+        uint64_t expect = v;
+        if (__hip_atomic_compare_exchange_strong(f, &expect, (a.epoch << 20) | (before + 1), __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          break;
+        v = expect;
+      }
+      g_merge = before + 1 == (uint64_t)a.n_groups;
+    } else {
+      __hip_atomic_store(&a.unit_flags[unit], stamp(a.epoch, t_end - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     for (int t = t_first; t < t_end; ++t)
       __hip_atomic_fetch_add(&a.done_count[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (tid == 0) {
+    g_merge = 0;
+  }
+  if (a.parallel_steps) {
+    // The group that counted in last merges every group's partial in group order (the
+    // result does not depend on which group finished last) and finalises.
+    __syncthreads();
+    if (g_merge && wave_rows) {
+      fence_acquire();
+      float m_tot = -INFINITY, l_tot = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+      for (int g = 0; g < a.n_groups; ++g) {
+        const float* pw = a.acc + (((int64_t)unit * a.n_groups + g) * kWaves + w) * (32 * D + 256);
+        const f32x4 ml = reinterpret_cast<const f32x4*>(pw + 32 * D)[lane];
+        const float mn = fmaxf(m_tot, ml[0]);
+        // A partial with no keys (-inf max) weighs zero; so does an empty running sum.
+        const float sa = m_tot == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_tot - mn);
+        const float sb = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - mn);
+        const f32x4* a4 = reinterpret_cast<const f32x4*>(pw);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const f32x4 v = a4[(db * 4 + gg) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db][gg * 4 + e] = fmaf(o[db][gg * 4 + e], sa, v[e] * sb);
+          }
+        l_tot = fmaf(l_tot, sa, ml[1] * sb);
+        m_tot = mn;
+      }
+      finalize_rows<D>(a, o, m_tot, l_tot, qrow, h, hi);
+    }
   }
 }
 
@@ -1252,7 +1314,8 @@ struct Sched {
 // read the same KV head share an L2. A workgroup takes from its own queue only while
 // that queue is at most one group ahead of the slowest queue, else from the slowest
 // queue. A task of group g needs its unit's group g-1 (claimed earlier, same queue
-// order) and staging of its steps, whose slots are released once every unit is past
+// order; not with parallel step groups, which need nothing of the unit's other groups)
+// and staging of its steps, whose slots are released once every unit is past
 // step group_end(g) - 1 - kSlots, which lies in group g-2 or earlier since no group has
 // more than kSlots/2 steps; every task of group g-2 is claimed
 // when the rule admits group

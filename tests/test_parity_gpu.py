@@ -143,6 +143,11 @@ SPLIT_VARIANTS = [
     dict(steps_per_task=4, grid_wgs=3),
     dict(steps_per_task=4, tail_steps=3, tail_steps_per_task=1),
     dict(steps_per_task=3, tail_steps=4, tail_steps_per_task=2, grid_wgs=5),
+    dict(parallel_steps=-1),
+    dict(parallel_steps=1, steps_per_task=1),
+    dict(parallel_steps=1, steps_per_task=2, grid_wgs=5),
+    dict(parallel_steps=1, steps_per_task=4, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+         stage_delay_ticks=3000),
 ]
 
 
@@ -223,26 +228,64 @@ def test_noncausal_rank_invariance():
 # --------------------------------------------------------------- protocol
 
 def test_bitwise_identical_across_splits_grids_and_delays():
+    """Within one mode the result bits do not depend on the staging split, the grid, the
+    timing or the controller. The default mode of this workload runs its step groups in
+    parallel (its units fill under half of the device), and that choice is the
+    device's, not the grid's."""
     cfg = CONFIGS[1]
     q, kv = make_inputs(cfg, seed=1)
     qg, kvg = q.cuda(), kv.cuda()
     announce("reference split")
     ref_o, ref_l = check_full(cfg, seed=1)
-    variants = [dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n) for n in (0, 1, 2, 4, 8, 32)]
-    variants += [dict(grid_wgs=g) for g in (1, 3, 8, 37)]
-    variants += [dict(stage_delay_ticks=2000), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
-                                                   stage_delay_ticks=5000)]
-    variants += [dict(initial_staging_wgs=16, controller_period_us=1)]
-    # Task sizes and tails: the blocks of a unit are processed in the same order with the
-    # same arithmetic whatever the grouping (the state between tasks is stored and
-    # reloaded exactly), so the results do not change either.
-    variants += [dict(steps_per_task=g, tail_steps=-1) for g in (1, 2, 3, 4)]
-    variants += [dict(steps_per_task=4, tail_steps=2, tail_steps_per_task=1),
-                 dict(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)]
-    for v in variants:
+    st = run_gpu(qg, kvg, cfg, want_stats=True)[2]
+    assert st["parallel_steps"] == 1, st
+    timing = [dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=n) for n in (0, 1, 2, 4, 8, 32)]
+    timing += [dict(grid_wgs=g) for g in (1, 3, 8, 37)]
+    timing += [dict(stage_delay_ticks=2000), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+                                                 stage_delay_ticks=5000)]
+    timing += [dict(initial_staging_wgs=16, controller_period_us=1), dict(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)]
+    for v in timing:
         announce(f"variant {v}")
         o, l = run_gpu(qg, kvg, cfg, **v)
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l), v
+    # Sequential mode: the blocks of a unit are processed in the same order with the
+    # same arithmetic whatever the grouping (the state between tasks is stored and
+    # reloaded exactly), so task sizes and tails do not change the bits either.
+    announce("sequential reference")
+    seq_o, seq_l = check_full(cfg, seed=1, parallel_steps=-1)
+    seq = [dict(steps_per_task=g, tail_steps=-1) for g in (1, 2, 3, 4)]
+    seq += [dict(steps_per_task=4, tail_steps=2, tail_steps_per_task=1), dict(grid_wgs=3), dict(grid_wgs=200)]
+    seq += timing[:2]
+    for v in seq:
+        announce(f"sequential variant {v}")
+        o, l = run_gpu(qg, kvg, cfg, parallel_steps=-1, **v)
+        assert torch.equal(o, seq_o) and torch.equal(l, seq_l), v
+    # Parallel mode with each grouping: the merge runs in group order, so a grouping's
+    # bits do not depend on which group finishes last (grids and staging splits vary).
+    for g in (1, 2, 3, 4):
+        announce(f"parallel grouping {g}")
+        po, pl = check_full(cfg, seed=1, parallel_steps=1, steps_per_task=g)
+        for v in (dict(grid_wgs=5), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=2, stage_delay_ticks=3000)):
+            o, l = run_gpu(qg, kvg, cfg, parallel_steps=1, steps_per_task=g, **v)
+            assert torch.equal(o, po) and torch.equal(l, pl), (g, v)
+
+
+def test_parallel_step_groups_reuse_slots():
+    """Twelve non-causal ring steps (each slot reused) with a unit's step groups run at
+    once and merged: every grouping and staging split matches the oracle, and the
+    parallel and sequential modes agree within the same bar."""
+    cfg = shape("par_reuse", 12, 5, 320, 320, 4, 2, 64, False)
+    for v in (dict(), dict(parallel_steps=1, steps_per_task=1), dict(parallel_steps=1, steps_per_task=3, grid_wgs=7),
+              dict(parallel_steps=1, steps_per_task=4, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1),
+              dict(parallel_steps=1, steps_per_task=2, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=3,
+                   stage_delay_ticks=4000),
+              dict(parallel_steps=-1)):
+        check_full(cfg, seed=21, **v)
+    q, kv = make_inputs(cfg, seed=21)
+    st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, parallel_steps=1, steps_per_task=2)[2]
+    print("    stats:", st, flush=True)
+    assert st["parallel_steps"] == 1 and st["step_groups"] == 6
+    assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]
 
 
 def test_back_to_back_launches_and_shape_changes():
@@ -326,7 +369,8 @@ def test_stats_and_controller_follow_eq2(mode, groups):
     split = mk.MK_SPLIT_ADAPTIVE if mode == "adaptive" else mk.MK_SPLIT_ADAPTIVE_PAPER
     g, tail_steps, tail_g = groups
     out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2,
-                           split_mode=split, steps_per_task=g, tail_steps=tail_steps, tail_steps_per_task=tail_g)
+                           split_mode=split, steps_per_task=g, tail_steps=tail_steps, tail_steps_per_task=tail_g,
+                           parallel_steps=-1)
     print("    stats:", st, flush=True)
     assert st["status"] == 0
     assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]

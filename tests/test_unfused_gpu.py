@@ -32,7 +32,8 @@ def both(cfg, q, kv, copy_wgs):
     l_u = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device="cuda")
     mk.mk_ring_attn_fwd_unfused(q, kv, cfg.n_chunks, cfg.rank, cfg.causal, cfg.gqa_ratio, o_u, l_u, copy, copy_wgs)
     o_f, l_f = mk.ring_attn_fwd(q, kv, cfg.rank, cfg.causal, cfg.gqa_ratio,
-                                opts=mk.default_opts(steps_per_task=1, tail_steps=-1, spin_timeout_us=TEST_TIMEOUT_US))
+                                opts=mk.default_opts(steps_per_task=1, tail_steps=-1, parallel_steps=-1,
+                                                     spin_timeout_us=TEST_TIMEOUT_US))
     torch.cuda.synchronize()
     mk.mk_ring_attn_status()
     return (o_u, l_u), (o_f, l_f)
