@@ -328,8 +328,9 @@ def run_ag(args):
     """One rank's AllGather+GEMM (C = A_full W^T after gathering the shards): the fused
     persistent kernel against the unfused baseline (the gather as one device copy, then
     the library GEMM, torch.matmul on hipBLASLt, on the same stream), over the gathered
-    sizes of Figure 4 (4K-32K rows, 8 ranks, K 8192, N 4096), with a staging split sweep
-    on the named workload. Prints one JSON line."""
+    sizes of the mKernel paper's AllGather+GEMM results (Figure 4: 4K-32K rows; here 8
+    ranks, K 8192, N 4096), with a staging split sweep on the named workload. Prints
+    one JSON line."""
     import torch
 
     import overlap_attention_amd as mk
