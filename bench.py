@@ -486,7 +486,7 @@ def _cpu_model():
     return "the host CPU"
 
 
-def oracle_timed(cfg, q, kv, rows):
+def oracle_timed(cfg, q, kv, rows, progress=False):
     """One timed pass of the fp64 oracle over `rows` (None: every row) of a workload,
     all heads: the oracle's own function, called once per KV head (a complete problem
     of its own), the KV heads spread over the cores of this process's affinity mask,
@@ -502,7 +502,7 @@ def oracle_timed(cfg, q, kv, rows):
     q64, kv64 = to_f64(q), to_f64(kv)
     rr = np.arange(cfg.lq) if rows is None else np.asarray(rows)
     t0 = time.perf_counter()
-    oracle_rows(oracle, q64, kv64, cfg.rank, cfg.causal, cfg.gqa_ratio, rr, workers=workers)
+    oracle_rows(oracle, q64, kv64, cfg.rank, cfg.causal, cfg.gqa_ratio, rr, workers=workers, progress=progress)
     dt = time.perf_counter() - t0
     if cfg.causal:
         pairs = int(sum(cfg.rank * cfg.lk + int(r) + 1 for r in rr))
@@ -539,10 +539,31 @@ def cpu_all_workloads():
              "| workload | rows | seconds | threads | algorithmic GFLOP/s |", "|---|---:|---:|---:|---:|"]
     for i, cfg in enumerate(CONFIGS):
         q, kv = make_inputs(cfg, seed=i)
-        dt, flops, workers = oracle_timed(cfg, q, kv, None)
+        dt, flops, workers = oracle_timed(cfg, q, kv, None, progress=True)
         log(f"[cpu] {cfg.name}: {dt:.1f} s, {flops / dt / 1e9:.1f} GFLOP/s on {workers} threads")
         lines.append(f"| {cfg.name} | {cfg.lq} | {dt:.2f} | {workers} | {flops / dt / 1e9:.1f} |")
         del q, kv
+    # The AllGather+GEMM oracle: one float64 product of the gathered shards, BLAS over
+    # the affinity mask's cores.
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from ag_inputs import AG_CONFIGS, make_ag_inputs
+    lines += ["", "| AllGather+GEMM workload | gathered rows | seconds | threads | algorithmic GFLOP/s |",
+              "|---|---:|---:|---:|---:|"]
+    cores = len(os.sched_getaffinity(0))
+    for cfg in AG_CONFIGS:
+        a, w = make_ag_inputs(cfg, seed=1)
+        a64, w64 = a.double().numpy(), w.double().numpy()
+        with threadpool_limits(cores):
+            t0 = time.perf_counter()
+            oracle.allgather_gemm_reference(a64, w64, cfg.rank)
+            dt = time.perf_counter() - t0
+        flops = 2.0 * cfg.m * cfg.n_out * cfg.k
+        log(f"[cpu] {cfg.name}: {dt:.1f} s, {flops / dt / 1e9:.1f} GFLOP/s on {cores} threads")
+        lines.append(f"| {cfg.name} | {cfg.m} | {dt:.2f} | {cores} | {flops / dt / 1e9:.1f} |")
+        del a, w, a64, w64
     return "\n".join(lines)
 
 
