@@ -442,7 +442,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
       } else {
         // Measured ticks averaged with the cost model's priors, weighted as one shard's
         // tasks of each role, so the first (cold) tasks do not swing the split.
-        const uint64_t kc = (uint64_t)a.n_rtiles * a.n_ntiles, ks = (uint64_t)a.n_chunks;
+        const uint64_t kc = (uint64_t)a.n_rtiles * a.n_ntiles, ks = (uint64_t)a.n_chunks * kPieces;
         cp = (int64_t)((ld64(&a.ctrl->compute_ticks.v) + kc * (uint64_t)a.cost_compute0) / (cd + kc));
         cs = (int64_t)((ld64(&a.ctrl->stage_ticks.v) + ks * (uint64_t)a.cost_stage0) / (sd + ks));
       }
