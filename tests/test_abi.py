@@ -106,6 +106,7 @@ int main(void) {
 def test_default_opts():
     o = mk.default_opts()
     assert o.split_mode == mk.MK_SPLIT_ADAPTIVE and o.grid_wgs == 0 and o.disable_staging == 0
+    assert o.parallel_steps == 0  # automatic: parallel step groups for launches with few units
 
 
 # ---------------------------------------------------------------- host validation
@@ -193,6 +194,9 @@ def test_negative_option_rejected():
     assert call(q, kv, 4, 1, 1, 4, o, l, opts) == mk.MK_E_INVAL
     opts = mk.default_opts(split_mode=7)
     assert call(q, kv, 4, 1, 1, 4, o, l, opts) == mk.MK_E_INVAL
+    for ps in (-2, 2):
+        assert call(q, kv, 4, 1, 1, 4, o, l, mk.default_opts(parallel_steps=ps)) == mk.MK_E_INVAL
+        assert b"parallel_steps" in mk.load_library().mk_last_error()
 
 
 def test_empty_query_is_a_noop():
