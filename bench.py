@@ -376,12 +376,41 @@ def run_ag(args):
             torch.matmul(a_full, w.t(), out=out)
         return f
 
+    gather_o = mk.ag_default_opts(phase=1)
+    gemm_o = mk.ag_default_opts(phase=2)
+
+    def same_code_fn(c, a, w, a_full, out):
+        # The unfused sequence of the fused kernel's own code: the gather, then the GEMM.
+        def f():
+            mk.mk_allgather_gemm_ex(a, c.n_ranks, c.rank, w, a_full, out, stream=stream, opts=gather_o)
+            mk.mk_allgather_gemm_ex(a, c.n_ranks, c.rank, w, a_full, out, stream=stream, opts=gemm_o)
+        return f
+
+    def gemm_only_ms(c, a, w, a_full, out, k):
+        # The GEMM phase alone: events around it, the gather before each outside them.
+        same_code_fn(c, a, w, a_full, out)()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(k):
+            mk.mk_allgather_gemm_ex(a, c.n_ranks, c.rank, w, a_full, out, stream=stream, opts=gather_o)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mk.mk_allgather_gemm_ex(a, c.n_ranks, c.rank, w, a_full, out, stream=stream, opts=gemm_o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / k
+
     a, w, a_full, out = setup(cfg)
     flops = 2 * cfg.m * cfg.n_out * cfg.k
     ms = timed(fused_fn(cfg, a, w, a_full, out), args.steps)
     mk.mk_ag_gemm_status(stream)
     st = mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, a_full, out, stream=stream, want_stats=True)
     ms_unf = timed(unfused_fn(cfg, a, w, a_full, out), args.steps)
+    ms_same = timed(same_code_fn(cfg, a, w, a_full, out), args.steps)
+    ms_gemm = gemm_only_ms(cfg, a, w, a_full, out, args.steps)
+    mk.mk_ag_gemm_status(stream)
+    log(f"[bench] ag unfused, same code: {ms_same:.4f} ms (GEMM phase alone {ms_gemm:.4f} ms)")
     tflops = flops / (ms * 1e-3) / 1e12
     clock = st["wg_cycles"] / st["wg_ticks"] * 0.1 if st["wg_ticks"] else None
     log(f"[bench] ag {cfg.name}: fused {ms:.4f} ms ({tflops:.1f} TFLOP/s), unfused {ms_unf:.4f} ms, stats {st}")
@@ -405,12 +434,15 @@ def run_ag(args):
             k = max(5, min(50, int(20 / (m / 16384))))
             t_f = timed(fused_fn(c, a, w, a_full, out), k)
             t_u = timed(unfused_fn(c, a, w, a_full, out), k)
+            t_s = timed(same_code_fn(c, a, w, a_full, out), k)
             mk.mk_ag_gemm_status(stream)
             sweep.append({"m": m, "fused_ms": round(t_f, 4), "unfused_ms": round(t_u, 4),
                           "unfused_over_fused": round(t_u / t_f, 3), "fused_tflops": round(f / t_f / 1e9, 1),
-                          "unfused_tflops": round(f / t_u / 1e9, 1)})
+                          "unfused_tflops": round(f / t_u / 1e9, 1), "unfused_same_code_ms": round(t_s, 4),
+                          "same_code_over_fused": round(t_s / t_f, 3)})
             log(f"[bench] ag M={m}: fused {t_f:.4f} ms ({f / t_f / 1e9:.1f} TFLOP/s), unfused {t_u:.4f} ms "
-                f"({f / t_u / 1e9:.1f} TFLOP/s), unfused/fused {t_u / t_f:.3f}")
+                f"({f / t_u / 1e9:.1f} TFLOP/s), unfused/fused {t_u / t_f:.3f}; same code unfused {t_s:.4f} ms "
+                f"({t_s / t_f:.3f}x fused)")
             del a, w, a_full, out
             torch.cuda.empty_cache()
     line = {
@@ -422,6 +454,9 @@ def run_ag(args):
                      "shader_clock_ghz": round(clock, 3) if clock else None},
         "unfused_baseline": {"what": "device copy of the shards into A_full, then torch.matmul (hipBLASLt)",
                              "ms": round(ms_unf, 4), "unfused_over_fused": round(ms_unf / ms, 3)},
+        "unfused_same_code": {"what": "the gather phase, then the GEMM phase of the same kernel (two launches)",
+                              "ms": round(ms_same, 4), "over_fused": round(ms_same / ms, 3),
+                              "gemm_phase_ms": round(ms_gemm, 4)},
         "split_sweep": {"ms": split, "best_fixed": best, "adaptive_over_best": round(split["adaptive"] / split[best], 3),
                         "adaptive_paper_over_best": round(split["adaptive_paper"] / split[best], 3)},
         "staging": {k: st[k] for k in ("grid_wgs", "staging_tasks", "assist_tasks", "max_staging_wgs")},

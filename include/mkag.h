@@ -47,7 +47,16 @@ typedef struct {
   int32_t grid_wgs;            /* 0 = one workgroup per resident slot (all CUs). */
   int64_t spin_timeout_us;     /* bound of every on-GPU wait; 0 = 10 s. */
   int32_t controller_period_us;/* minimum time between controller updates; 0 = 20 us. */
-  int32_t reserved[5];
+  int32_t phase;               /* 0: the fused call. The unfused sequence of the same code
+                                  ([P] Fig. 1(b): the gather, then the GEMM, released at
+                                  the kernel boundary) for measurement: 1 runs the gather
+                                  only (every workgroup stages; a_full and the chunk
+                                  flags are written, c is not); 2 runs the GEMM only,
+                                  consuming the chunk flags of the phase-1 call just
+                                  before it on the same stream, which must have had the
+                                  same arguments (MK_E_INVAL if no phase-1 call
+                                  precedes it). */
+  int32_t reserved[4];
 } mk_ag_gemm_opts;
 
 /* Filled by mk_allgather_gemm_ex when stats != NULL (the call then synchronises the

@@ -94,7 +94,8 @@ class mk_ag_gemm_opts(ctypes.Structure):
         ("grid_wgs", ctypes.c_int32),
         ("spin_timeout_us", ctypes.c_int64),
         ("controller_period_us", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("phase", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
 

@@ -39,6 +39,8 @@ struct Workspace {
   mkag::Status* status = nullptr;
   uint64_t* flags = nullptr;
   size_t flags_cap = 0;
+  uint64_t gathered_epoch = 0;  // epoch of a phase-1 call not yet consumed by phase 2
+  uint64_t gathered_sig[8] = {};  // that call's tensors and shape
 };
 
 std::mutex g_mu;
@@ -144,6 +146,7 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
   if (opts.fixed_staging_wgs < 0 || opts.initial_staging_wgs < 0 || opts.grid_wgs < 0 || opts.spin_timeout_us < 0 ||
       opts.controller_period_us < 0)
     return fail(MK_E_INVAL, "negative option");
+  if (opts.phase < 0 || opts.phase > 2) return fail(MK_E_INVAL, "opts.phase must be 0, 1 or 2");
   if (m_loc == 0) {
     if (stats != nullptr) std::memset(stats, 0, sizeof(*stats));
     return MK_OK;  // nothing to gather or compute
@@ -250,7 +253,32 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
   a.flags = ws->flags;
   a.ctrl = ws->ctrl;
   a.status = ws->status;
-  a.epoch = ++ws->epoch;
+  // Unfused phases: the gather stages every chunk with every workgroup and computes
+  // nothing; the GEMM stages nothing and consumes the flags the gather just stamped,
+  // under the gather's epoch.
+  const uint64_t sig[8] = {(uint64_t)(uintptr_t)a.a_shards, (uint64_t)(uintptr_t)a.a_full, (uint64_t)(uintptr_t)a.w,
+                           (uint64_t)(uintptr_t)a.c, (uint64_t)n, (uint64_t)m_loc, (uint64_t)k,
+                           ((uint64_t)n_out << 32) | (uint32_t)rank};
+  if (opts.phase == 1) {
+    std::memcpy(ws->gathered_sig, sig, sizeof(sig));
+    for (int x = 0; x < a.n_xcd; ++x) a.xcd_ntiles[x] = 0;
+    a.n_compute = 0;
+    a.split_fixed = 1;
+    a.initial_stagers = grid;
+    a.epoch = ++ws->epoch;
+    ws->gathered_epoch = a.epoch;
+  } else if (opts.phase == 2) {
+    if (ws->gathered_epoch == 0 || ws->gathered_epoch != ws->epoch ||
+        std::memcmp(ws->gathered_sig, sig, sizeof(sig)) != 0)
+      return fail(MK_E_INVAL, "opts.phase 2 needs a phase-1 call with the same arguments just before it on this stream");
+    a.n_stage_tasks = 0;
+    a.split_fixed = 1;
+    a.initial_stagers = 0;
+    a.epoch = ws->epoch;
+    ws->gathered_epoch = 0;
+  } else {
+    a.epoch = ++ws->epoch;
+  }
   if ((e = mkag_kernel_launch(&a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
 
   if (stats != nullptr) {

@@ -520,7 +520,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
     const int need =
         ((p - 1) * a.n_chunks + min(kChunksPerTile * jj + kChunksPerTile - 1, a.n_chunks - 1)) * kPieces + kPieces - 1;
     uint32_t h = ld32(&a.ctrl->stage_head.v);
-    while ((int)h <= need) {
+    while ((int)h <= need && (int)h < a.n_stage_tasks) {
       uint32_t expect = h;
       if (__hip_atomic_compare_exchange_strong(&a.ctrl->stage_head.v, &expect, h + 1, __ATOMIC_RELAXED,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {

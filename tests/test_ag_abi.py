@@ -58,6 +58,9 @@ def test_bad_options():
     a, w, f, c = good()
     assert call(a, 4, 1, w, f, c, mk.ag_default_opts(grid_wgs=-1)) == mk.MK_E_INVAL
     assert call(a, 4, 1, w, f, c, mk.ag_default_opts(split_mode=9)) == mk.MK_E_INVAL
+    for ph in (-1, 3):
+        assert call(a, 4, 1, w, f, c, mk.ag_default_opts(phase=ph)) == mk.MK_E_INVAL
+        assert b"phase" in mk.load_library().mk_last_error()
 
 
 def test_empty_shards_are_a_noop():

@@ -111,6 +111,39 @@ def test_stale_flags_of_previous_launch_are_not_consumed():
     assert rep["ok"], fmt(rep)
 
 
+def test_unfused_phases_equal_the_fused_call():
+    """The unfused sequence of the same code (gather, then GEMM, two launches on one
+    stream) writes the fused call's bits; a GEMM phase without its gather, or after a
+    gather with other arguments, is refused on the host."""
+    cfg = AgConfig("phases_r1of4_M320_K256_N768", n_ranks=4, rank=1, m_loc=320, k=256, n_out=768)
+    a, w = make_ag_inputs(cfg, 11)
+    a, w = a.cuda(), w.cuda()
+    announce("fused reference")
+    ref_full, ref_c = check(cfg, seed=11)
+    f = torch.empty((cfg.m, cfg.k), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((cfg.m, cfg.n_out), dtype=torch.bfloat16, device="cuda")
+    for g in (0, 5):
+        announce(f"phases, grid {g}")
+        f.zero_()
+        c.zero_()
+        mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, f, c, opts=opts(phase=1, grid_wgs=g))
+        torch.cuda.synchronize()
+        assert torch.equal(f, ref_full) and not c.any(), "the gather phase writes A_full only"
+        mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, f, c, opts=opts(phase=2, grid_wgs=g))
+        torch.cuda.synchronize()
+        mk.mk_ag_gemm_status()
+        assert torch.equal(f, ref_full) and torch.equal(c, ref_c), g
+    announce("GEMM phase without its gather")
+    with pytest.raises(RuntimeError):
+        mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, f, c, opts=opts(phase=2))
+    mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, f, c, opts=opts(phase=1))
+    other = torch.zeros_like(c)
+    with pytest.raises(RuntimeError):
+        mk.mk_allgather_gemm_ex(a, cfg.n_ranks, cfg.rank, w, f, other, opts=opts(phase=2))
+    torch.cuda.synchronize()
+    mk.mk_ag_gemm_status()
+
+
 def test_stats_count_every_task():
     cfg = AgConfig("stats_r1of8_M256_K256_N1024", n_ranks=8, rank=1, m_loc=256, k=256, n_out=1024)
     a, w = make_ag_inputs(cfg, 9)
