@@ -288,6 +288,19 @@ def test_parallel_step_groups_reuse_slots():
     assert st["compute_tasks_done"] == st["n_units"] * st["n_steps"]
 
 
+def test_parallel_step_groups_causal_gqa():
+    """Causal GQA, rank 9 of 10 (ten steps, slots reused, the diagonal step in group 0):
+    parallel groups of every size and a ragged head dim 128 query block, against the
+    oracle; the default mode is parallel here."""
+    cfg = shape("par_causal_gqa", 10, 9, 200, 200, 8, 2, 128, True)
+    q, kv = make_inputs(cfg, seed=23)
+    st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True)[2]
+    assert st["parallel_steps"] == 1, st
+    for v in (dict(), dict(steps_per_task=1), dict(steps_per_task=3, grid_wgs=6),
+              dict(steps_per_task=4, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=2, stage_delay_ticks=3000)):
+        check_full(cfg, seed=23, parallel_steps=1, **v)
+
+
 def test_back_to_back_launches_and_shape_changes():
     a = CONFIGS[1]
     b = shape("other", 5, 3, 300, 300, 8, 2, 64, True)
