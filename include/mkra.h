@@ -14,7 +14,8 @@
  * unit) take one of two roles: compute (the attention steps) or staging (the ring
  * receive: copy each step's KV chunk into a ring of eight slots in HBM, 128-row tile
  * by 128-row tile, in the layout the compute role reads, and publish an
- * epoch-stamped ready flag per tile). An on-GPU controller re-targets the number of staging
+ * epoch-stamped ready flag per tile, or per range of a tile's KV heads when the tile
+ * is staged in pieces). An on-GPU controller re-targets the number of staging
  * workgroups with Eq. (2).
  *
  * Conventions for every entry point:
@@ -128,7 +129,16 @@ typedef struct {
                                   clamped to 2..4, and there is no default tail.
                                   Results are reproducible for a given mode and
                                   grouping (the merge runs in group order). */
-  int32_t reserved;
+  int32_t stage_pieces;        /* staging tasks per 128-row tile: its KV heads split
+                                  into this many ranges of ceil(Hkv / stage_pieces)
+                                  heads (fewer when that divides Hkv into fewer
+                                  ranges), each range staged by one task and published
+                                  by its own ready flag, which the units of those
+                                  heads alone wait for. 1..Hkv (larger values are
+                                  clamped to Hkv); 0 = default (set by the library
+                                  from the problem's size, see
+                                  mk_ring_attn_stats.stage_pieces). Results do not
+                                  depend on it. */
 } mk_ring_attn_opts;
 
 /* Filled by mk_ring_attn_fwd_ex when stats != NULL (the call then synchronises the
@@ -140,8 +150,8 @@ typedef struct {
   int32_t n_units;             /* compute units per step (head group x query block) */
   int32_t n_steps;             /* ring steps run */
   int32_t n_stage_tiles;       /* 128-row staged tiles per chunk */
-  int32_t n_stage_tasks;       /* staging tasks in total: one per (step, tile); the
-                                  local chunk of step 0 is staged too */
+  int32_t n_stage_tasks;       /* staging tasks in total: one per (step, tile, piece);
+                                  the local chunk of step 0 is staged too */
   int32_t compute_tasks_done;
   int32_t staging_tasks_done;  /* by staging and by compute workgroups */
   int32_t assist_tasks;        /* staging tasks done by compute workgroups whose input
@@ -167,13 +177,14 @@ typedef struct {
   int32_t step_groups;         /* compute tasks per unit */
   int32_t parallel_steps;      /* 1 if the launch ran its step groups at once (see
                                   mk_ring_attn_opts.parallel_steps) */
-  int32_t reserved;
+  int32_t stage_pieces;        /* staging tasks per tile in this launch (see
+                                  mk_ring_attn_opts.stage_pieces) */
 } mk_ring_attn_stats;
 
 /* One trace record (64 bytes). kind: 1 compute task (v0 unit, v1 step, v2 start tick,
  * v3 wait ticks), 2 staging task (v0 task, v1 step, v2 tile, v3 start tick, v4 1 if
- * done by a stalled compute workgroup, v5 element offset of its destination in the
- * slot ring, -1 if it did not copy), 3 controller update (v0 R_p as Eq. (2) takes it:
+ * done by a stalled compute workgroup, v5 its piece of the tile, -1 if it did not
+ * copy), 3 controller update (v0 R_p as Eq. (2) takes it:
  * unclaimed compute unit-steps, less the last ring step's in ADAPTIVE mode, v1 R_s, v2 C_p,
  * v3 C_s, v4 blocks B, v5 new target), 4 role switch (v0 new role: 0 compute,
  * 1 staging, v1 staging-role count after it). t: tick at which it was written. */

@@ -47,7 +47,7 @@ class mk_ring_attn_opts(ctypes.Structure):
         ("tail_steps", ctypes.c_int32),
         ("tail_steps_per_task", ctypes.c_int32),
         ("parallel_steps", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("stage_pieces", ctypes.c_int32),
     ]
 
 
@@ -79,7 +79,7 @@ class mk_ring_attn_stats(ctypes.Structure):
         ("steps_per_task", ctypes.c_int32),
         ("step_groups", ctypes.c_int32),
         ("parallel_steps", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("stage_pieces", ctypes.c_int32),
     ]
 
     def as_dict(self):

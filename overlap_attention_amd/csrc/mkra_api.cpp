@@ -215,6 +215,17 @@ constexpr int kDefaultTailStepsPerTask = 2;
 constexpr int kDefaultTailSteps = 4;
 int default_steps_per_task(int64_t lk, int64_t d) { return lk * d >= (int64_t(1) << 19) ? 2 : 4; }
 
+// Staging pieces per tile when opts.stage_pieces is 0: two when a step has few tiles
+// (at most 8: the first tiles' staging latency is on the critical path of a short
+// launch, and two pieces let two workgroups stage a tile at once) or a tile is large
+// (>= 1 MB), else one. Measured on the 1K-token MHA workload (8 tiles of 1 MB), the
+// 6K-24K-token GQA rings (3-12 tiles of 512 KB) and the 32K-token D = 64 ring (16
+// tiles of 2 MB): more pieces than this add per-task costs (the slot check, the
+// publish) that outweigh the parallelism.
+int default_stage_pieces(int64_t n_tiles, int64_t tile_bytes) {
+  return (n_tiles <= 8 || tile_bytes >= (int64_t(1) << 20)) ? 2 : 1;
+}
+
 
 // Largest divisor of g that divides the wave count: query heads per unit.
 int heads_per_unit(int g) {
@@ -293,7 +304,7 @@ mk_status launch_unfused(const mkra::KernelArgs& a, Workspace* w, hipStream_t st
   st.n_xcd = 1;
   for (int x = 0; x <= mkra::kMaxXcd; ++x) st.xcd_unit_begin[x] = 0;
   st.n_groups = 0;  // no compute task
-  st.n_stage_tasks = a.n_tiles;
+  st.n_stage_tasks = a.stage_per_step;
   st.split_fixed = 1;
   st.initial_stagers = n_copy;
   st.disable_staging = 0;
@@ -326,7 +337,7 @@ mk_status launch_unfused(const mkra::KernelArgs& a, Workspace* w, hipStream_t st
   for (int t = 0; t < n_steps; ++t) {
     if (t >= mkra::kSlots && (e = hipStreamWaitEvent(copy_stream, w->ev_computed[t - mkra::kSlots], 0)) != hipSuccess)
       return hip_fail(e, "event wait");
-    st.stage_lo = t * a.n_tiles;
+    st.stage_lo = t * a.stage_per_step;
     if ((e = mkra_kernel_launch(&st, copy_stream)) != hipSuccess) return hip_fail(e, "kernel launch");
     if ((e = hipEventRecord(w->ev_staged[t], copy_stream)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(stream, w->ev_staged[t], 0)) != hipSuccess) return hip_fail(e, "event wait");
@@ -380,6 +391,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     return fail(MK_E_INVAL, "opts.tail_steps_per_task must be 0 (default) or 1..4");
   if (opts.parallel_steps < -1 || opts.parallel_steps > 1)
     return fail(MK_E_INVAL, "opts.parallel_steps must be -1, 0 or 1");
+  if (opts.stage_pieces < 0) return fail(MK_E_INVAL, "opts.stage_pieces must be 0 (default) or positive");
   if (opts.fixed_staging_wgs < 0 || opts.initial_staging_wgs < 0 || opts.grid_wgs < 0 || opts.spin_timeout_us < 0 ||
       opts.controller_period_us < 0 || opts.trace_capacity < 0 || opts.stage_delay_ticks < 0)
     return fail(MK_E_INVAL, "negative option");
@@ -415,9 +427,20 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   // blocks (keys past Lk as zeros), so a compute phase of two blocks (D = 64) never
   // reaches past its head's blocks.
   a.n_blocks = a.n_tiles * (mkra::kStageRows / mkra::kBN);
+  // A tile's KV heads in pieces of piece_heads heads, one staging task and one ready
+  // flag each.
+  {
+    const int64_t tile_bytes = 2 * 2 * std::min<int64_t>(mkra::kStageRows, lk) * hkv * d;
+    const int pieces = (int)std::min<int64_t>(
+        hkv, opts.stage_pieces > 0 ? opts.stage_pieces : default_stage_pieces(a.n_tiles, tile_bytes));
+    a.piece_heads = (int)((hkv + pieces - 1) / pieces);
+    a.n_pieces = (int)((hkv + a.piece_heads - 1) / a.piece_heads);
+  }
+  if ((int64_t)a.n_tiles * a.n_pieces > (int64_t)INT32_MAX / 2) return fail(MK_E_INVAL, "too many staging tasks");
+  a.stage_per_step = a.n_tiles * a.n_pieces;
   // Every step's chunk, the local one included, is staged once into the layout the
   // compute role reads.
-  const int64_t n_stage_tasks = (int64_t)n_steps * a.n_tiles;
+  const int64_t n_stage_tasks = (int64_t)n_steps * a.stage_per_step;
   if (n_stage_tasks > (int64_t)INT32_MAX - 1) return fail(MK_E_INVAL, "too many staging tasks");
   a.n_stage_tasks = (int)n_stage_tasks;
   a.chunk_elems = 2 * lk * hkv * d;
@@ -490,8 +513,8 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   const double task_flops = 4.0 * d * (a.hg * a.bq) * (double)lk;
   const double cu_rate = 0.5 * 4096.0 * 2.4e9;
   a.cost_compute0 = std::max<int64_t>(1, (int64_t)(task_flops / cu_rate * 1e8));
-  const double tile_bytes = 2.0 * 2.0 * 2.0 * (double)std::min<int64_t>(mkra::kStageRows, lk) * hkv * d;
-  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(tile_bytes / 40e9 * 1e8));
+  const double piece_bytes = 2.0 * 2.0 * 2.0 * (double)std::min<int64_t>(mkra::kStageRows, lk) * a.piece_heads * d;
+  a.cost_stage0 = std::max<int64_t>(1, (int64_t)(piece_bytes / 40e9 * 1e8));
   a.split_fixed = opts.split_mode == MK_SPLIT_FIXED ? 1 : 0;
   a.ctrl_paper = opts.split_mode == MK_SPLIT_ADAPTIVE_PAPER ? 1 : 0;
   a.disable_staging = opts.disable_staging ? 1 : 0;
@@ -522,7 +545,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     const uint64_t o_ctrl = align256(sizeof(DevStatus));
     const uint64_t o_done = o_ctrl + align256(sizeof(DevCtrl));
     const uint64_t o_sflags = o_done + align256((uint64_t)n_steps * sizeof(uint32_t));
-    const uint64_t o_uflags = o_sflags + align256((uint64_t)mkra::kSlots * a.n_tiles * sizeof(uint64_t));
+    const uint64_t o_uflags = o_sflags + align256((uint64_t)mkra::kSlots * a.stage_per_step * sizeof(uint64_t));
     const uint64_t o_slots = o_uflags + align256((uint64_t)n_units * sizeof(uint64_t));
     const uint64_t o_acc = o_slots + align256((uint64_t)mkra::kSlots * a.slot_bytes + mkra::kDiscardBytes);
     const uint64_t need =
@@ -572,7 +595,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     if ((e = hipMemsetAsync(w->status, 0, sizeof(DevStatus), stream)) != hipSuccess) return hip_fail(e, "memset");
   }
   GROW(done_count, w->done_cap, n_steps, true);
-  GROW(slot_flags, w->tiles_cap, mkra::kSlots * (size_t)a.n_tiles, true);
+  GROW(slot_flags, w->tiles_cap, mkra::kSlots * (size_t)a.stage_per_step, true);
   GROW(unit_flags, w->units_cap, n_units, true);
   // The ring slots, then one block of scratch that the compute role's discarded copies
   // read (its contents are never used).
@@ -602,10 +625,10 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     // launch, a stamp of the right step but of the previous or the next launch (even
     // and odd entries). The kernel must consume none of them.
     auto stamp = [](uint64_t ep, int step) { return (ep << 20) | (uint64_t)(step + 1); };
-    std::vector<uint64_t> sf((size_t)mkra::kSlots * a.n_tiles), uf((size_t)n_units);
+    std::vector<uint64_t> sf((size_t)mkra::kSlots * a.stage_per_step), uf((size_t)n_units);
     for (int sl = 0; sl < mkra::kSlots; ++sl)
-      for (int j = 0; j < a.n_tiles; ++j)
-        sf[(size_t)sl * a.n_tiles + j] = stamp(((sl + j) & 1) ? a.epoch + 1 : a.epoch - 1, sl);
+      for (int j = 0; j < a.stage_per_step; ++j)
+        sf[(size_t)sl * a.stage_per_step + j] = stamp(((sl + j) & 1) ? a.epoch + 1 : a.epoch - 1, sl);
     for (int64_t u = 0; u < n_units; ++u)
       uf[(size_t)u] = stamp((u & 1) ? a.epoch + 1 : a.epoch - 1, (int)(u % n_steps));
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -631,6 +654,7 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
     stats->n_steps = n_steps;
     stats->n_stage_tiles = a.n_tiles;
     stats->n_stage_tasks = a.n_stage_tasks;
+    stats->stage_pieces = a.n_pieces;
     stats->compute_tasks_done = ds.compute_done;
     stats->staging_tasks_done = ds.stage_done;
     stats->assist_tasks = ds.assist_tasks;

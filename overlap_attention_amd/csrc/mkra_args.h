@@ -14,7 +14,8 @@ constexpr int kRowsPerWave = 32;
 // Keys per KV block held in LDS (a ring of kStages blocks).
 constexpr int kBN = 64;
 // Rows of a staged KV tile: the pages' Table 3 moves Ring Attention's KV in tiles of
-// 128 rows; one staging task and one ready flag per (slot, tile).
+// 128 rows. A tile's KV heads may be split into pieces (ranges of heads); one staging
+// task and one ready flag per (slot, tile, piece).
 constexpr int kStageRows = 128;
 // LDS pipeline depth of the compute role: KV blocks in flight per workgroup.
 constexpr int kStages = 4;
@@ -160,17 +161,21 @@ struct KernelArgs {
   int n_xcd;              // compute queues (one per XCD)
   int xcd_unit_begin[kMaxXcd + 1];
 
-  // Staging work: tasks = (step 0..S-1) x (128-row tile); each step's chunk is staged
+  // Staging work: tasks = (step 0..S-1) x (128-row tile) x (piece: piece_heads KV
+  // heads, the last piece possibly fewer), in that order; each step's chunk is staged
   // into slot step % kSlots as blocks of 64 keys per KV head.
   int n_tiles;            // ceil(Lk / 128)
   int n_blocks;           // 2 * n_tiles: blocks per KV head (keys past Lk staged as zeros)
+  int n_pieces;           // ceil(Hkv / piece_heads)
+  int piece_heads;        // KV heads per piece
+  int stage_per_step;     // n_tiles * n_pieces: staging tasks (and ready flags) per step
   int n_stage_tasks;
   int64_t chunk_elems;    // 2 * Lk * Hkv * D: one chunk in kv_chunks
   int64_t slot_bytes;     // Hkv * n_blocks * block bytes
 
   // Workspace (library-owned device memory).
   uint8_t* slots;         // [kSlots][Hkv][n_blocks] staged blocks, then kDiscardBytes
-  uint64_t* slot_flags;   // [kSlots][n_tiles] epoch-stamped ready flags
+  uint64_t* slot_flags;   // [kSlots][n_tiles][n_pieces] epoch-stamped ready flags
   uint64_t* unit_flags;   // [n_units] epoch-stamped "step done" per unit
   float* acc;             // [n_units][kWaves][32*D + 256] running (O, m, l, lr) between steps
   uint32_t* done_count;   // [n_steps] units finished per step (slot release)
@@ -189,7 +194,7 @@ struct KernelArgs {
   int stage_delay_ticks;
   int debug_flags;        // bit 0: a staging workgroup reads back the K it wrote
   int64_t cost_compute0;  // modelled ticks per compute task (controller prior)
-  int64_t cost_stage0;    // modelled ticks per staging task (one tile)
+  int64_t cost_stage0;    // modelled ticks per staging task (one piece of a tile)
   uint64_t timeout_ticks;
   uint64_t ctrl_period_ticks;
 };

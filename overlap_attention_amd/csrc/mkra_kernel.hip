@@ -221,9 +221,9 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   uint64_t sd = ld32(&a.ctrl->stage_done.v),
            stt = ld64(&a.ctrl->stage_ticks.v) + ld64(&a.ctrl->stage_wait_ticks.v);
   // The cost-model priors count as one ring step's tasks of each role (n_units
-  // compute unit-steps, n_tiles staging tiles), so the first few measured tasks (cold
-  // caches, no slot waits yet) do not swing the split.
-  const uint64_t kc = (uint64_t)a.n_units, ks = (uint64_t)a.n_tiles;
+  // compute unit-steps, stage_per_step staging tasks), so the first few measured tasks
+  // (cold caches, no slot waits yet) do not swing the split.
+  const uint64_t kc = (uint64_t)a.n_units, ks = (uint64_t)a.stage_per_step;
   int64_t cp, cs, rp2;
   if (a.ctrl_paper) {
     // Eq. (2) with the inputs §3.2 names: every remaining task of each role and the
@@ -407,12 +407,12 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // ------------------------------------------------------------------ staging role
 
-// One staging task, run by the whole workgroup: 128-row tile j of the chunk of step
-// t (chunk (rank - t) mod N, read from its home in kv_chunks, which stands for the
-// predecessor's memory) becomes staged blocks in slot t % kSlots: K swizzled, V
-// transposed to fp16. The slot is free once every unit has finished step t - kSlots.
-// One release per
-// tile publishes its epoch-stamped flag (paper §4: epoch-stamped readiness flags).
+// One staging task, run by the whole workgroup: piece pc (KV heads [pc*piece_heads,
+// +piece_heads)) of 128-row tile j of the chunk of step t (chunk (rank - t) mod N, read
+// from its home in kv_chunks, which stands for the predecessor's memory) becomes
+// staged blocks in slot t % kSlots: K swizzled, V transposed to fp16. The slot is free
+// once every unit has finished step t - kSlots. One release per piece publishes its
+// epoch-stamped flag (paper §4: epoch-stamped readiness flags).
 template <int D>
 __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs* ap, uint32_t k, bool assist) {
   constexpr int CPR = D / 8;                        // 16-byte chunks per K/V row
@@ -422,8 +422,10 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
   static_assert(KCH >= 1 && kBN * CPR % kThreads == 0, "block split");
   const int tid = threadIdx.x, lane = tid & 63;
   const uint64_t t_begin = ticks();
-  const int t = (int)k / a.n_tiles;
-  const int j = (int)k % a.n_tiles;
+  const int t = (int)k / a.stage_per_step;
+  const int j = ((int)k % a.stage_per_step) / a.n_pieces;
+  const int pc = (int)k % a.n_pieces;
+  const int g0 = pc * a.piece_heads;               // first KV head of the piece
   const int slot = t % kSlots;
   uint64_t w = 0;
   // Slot release (every wave waits; a timeout leaves the error word set for all).
@@ -438,13 +440,13 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
     const uint16_t* vh = kh + (int64_t)a.lk * row_elems;
     uint8_t* sbase = a.slots + (int64_t)slot * a.slot_bytes;
     const int nb = min(2, a.n_blocks - 2 * j);       // 64-key blocks in this tile
-    const int n_pairs = a.hkv * nb;
+    const int n_pairs = min(a.piece_heads, a.hkv - g0) * nb;
     for (int p0 = 0; p0 < n_pairs; p0 += NB) {
       u32x4 kr[NB][KCH], vr[NB][KCH];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int p = p0 + b;
-        const int g = p / nb, kb = 2 * j + p % nb;
+        const int g = g0 + p / nb, kb = 2 * j + p % nb;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
           const int q = tid + i * kThreads, r = q / CPR, cc = q % CPR, key = kb * kBN + r;
@@ -459,7 +461,7 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
       for (int b = 0; b < NB; ++b) {
         const int p = p0 + b;
         if (p >= n_pairs) break;
-        const int g = p / nb, kb = 2 * j + p % nb;
+        const int g = g0 + p / nb, kb = 2 * j + p % nb;
         uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
@@ -482,7 +484,7 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
       for (int b = 0; b < NB; ++b) {
         const int p = p0 + b;
         if (p >= n_pairs) break;
-        const int g = p / nb, kb = 2 * j + p % nb;
+        const int g = g0 + p / nb, kb = 2 * j + p % nb;
         uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes + Block<D>::kKBytes;
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(scr[b]);
         for (int q = tid; q < D * 8; q += kThreads) {
@@ -504,7 +506,7 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
       // Debug: re-derive the K part of every block of the tile from the chunk's home.
       uint32_t bad = 0;
       for (int p = 0; p < n_pairs; ++p) {
-        const int g = p / nb, kb = 2 * j + p % nb;
+        const int g = g0 + p / nb, kb = 2 * j + p % nb;
         const uint8_t* blk = sbase + ((int64_t)g * a.n_blocks + kb) * Block<D>::kBytes;
         for (int q = tid; q < kBN * CPR; q += kThreads) {
           const int r = q / CPR, cc = q % CPR, key = kb * kBN + r;
@@ -530,13 +532,14 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (tid == 0) {
-    if (ok && !v_range) st64_release(&a.slot_flags[slot * a.n_tiles + j], stamp(a.epoch, t));
+    if (ok && !v_range) st64_release(&a.slot_flags[(int64_t)slot * a.stage_per_step + (int)k % a.stage_per_step],
+                                     stamp(a.epoch, t));
     const uint64_t busy = ticks() - t_begin - w;
     add64(&a.ctrl->stage_ticks.v, busy);
     add32(&a.ctrl->stage_done.v, 1);
     add64(&a.ctrl->stage_wait_ticks.v, w);
     if (assist) add32(&a.ctrl->assist_tasks.v, 1);
-    if (a.trace != nullptr) trace_rec(ap, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? 1 : -1);
+    if (a.trace != nullptr) trace_rec(ap, kTraceStage, k, t, j, (int64_t)t_begin, assist ? 1 : 0, ok ? pc : -1);
   }
   (void)lane;
 }
@@ -721,20 +724,20 @@ __device__ __forceinline__ const uint8_t* task_slot_ptr(const KernelArgs& a, int
   return wave_bcast_ptr(a.slots + (int64_t)((uint32_t)t % (uint32_t)kSlots) * a.slot_bytes + head_off);
 }
 
-// The ready flags of the tiles of step t.
-__device__ __forceinline__ const uint64_t* step_flags(const KernelArgs& a, int t) {
-  return a.slot_flags + ((uint32_t)t % (uint32_t)kSlots) * a.n_tiles;
+// The ready flag of piece pc of tile 0 of step t; tile j's is n_pieces * j further.
+__device__ __forceinline__ const uint64_t* step_flags(const KernelArgs& a, int t, int pc) {
+  return a.slot_flags + ((uint32_t)t % (uint32_t)kSlots) * a.stage_per_step + pc;
 }
 
 // Tile gi of a task's tile sequence (the tiles of its steps in order: nt0 of the first
-// step starting at t_first, ntf of each later one; at most four steps): its flag and
-// the stamp that flag holds once the tile is staged.
-__device__ __forceinline__ void task_tile_flag(const KernelArgs& a, int t_first, int nt0, int ntf, int gi,
+// step starting at t_first, ntf of each later one; at most four steps): the flag of its
+// piece pc and the stamp that flag holds once the piece is staged.
+__device__ __forceinline__ void task_tile_flag(const KernelArgs& a, int t_first, int nt0, int ntf, int gi, int pc,
                                                const uint64_t*& f, uint64_t& want) {
   static_assert(kMaxGroup <= 4, "three boundaries tell four steps apart");
   const int st = (int)(gi >= nt0) + (int)(gi >= nt0 + ntf) + (int)(gi >= nt0 + 2 * ntf);
   const int t = t_first + st;
-  f = step_flags(a, t) + (gi - (st == 0 ? 0 : nt0 + (st - 1) * ntf));
+  f = step_flags(a, t, pc) + (gi - (st == 0 ? 0 : nt0 + (st - 1) * ntf)) * a.n_pieces;
   want = stamp(a.epoch, t);
 }
 
@@ -786,6 +789,7 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   const int t_first = group_first(a, step_group), t_end = group_end(a, step_group);
   const int p = unit / a.n_qblocks, qb = unit % a.n_qblocks;
   const int kvh = p / a.n_hgroups, hgi = p % a.n_hgroups;
+  const int pc = kvh / a.piece_heads;  // the staging piece that holds this KV head
   const int h = kvh * a.gqa + hgi * a.hg + (w % a.hg);
   const int q0w = qb * a.bq + (w / a.hg) * kRowsPerWave;
   const bool wave_rows = q0w < a.lq;
@@ -878,13 +882,13 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
     const uint64_t* f;
     uint64_t want;
     if (lane < 63 && lane < n_task_tiles) {
-      task_tile_flag(a, t_first, nt0, ntf, lane, f, want);
+      task_tile_flag(a, t_first, nt0, ntf, lane, pc, f, want);
       r0 = ld64(f) == want;
     } else if (lane == 63 && t_first > 0 && !a.parallel_steps) {
       r0 = ld64(&a.unit_flags[unit]) == stamp(a.epoch, t_first - 1);
     }
     if (63 + lane < n_task_tiles) {
-      task_tile_flag(a, t_first, nt0, ntf, 63 + lane, f, want);
+      task_tile_flag(a, t_first, nt0, ntf, 63 + lane, pc, f, want);
       r1 = ld64(f) == want;
     }
     const uint64_t nr0 = __ballot(!r0), nr1 = __ballot(!r1);
@@ -955,14 +959,14 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
       // Wait for this tile's flag, then look at the later flags of the task's tile
       // sequence 64 at a time (one load per lane) so the next tiles need no check.
       const int t = t_first + cst;
-      ok &= wave_wait_stamp(a, step_flags(a, t) + cb / kBlocksPerTile, stamp(a.epoch, t), waited);
+      ok &= wave_wait_stamp(a, step_flags(a, t, pc) + (cb / kBlocksPerTile) * a.n_pieces, stamp(a.epoch, t), waited);
       int upto = ctile + 1;
       for (int g0 = ctile + 1; g0 < n_task_tiles; g0 += 64) {
         bool ready = false;
         if (g0 + lane < n_task_tiles) {
           const uint64_t* f;
           uint64_t want;
-          task_tile_flag(a, t_first, nt0, ntf, g0 + lane, f, want);
+          task_tile_flag(a, t_first, nt0, ntf, g0 + lane, pc, f, want);
           ready = ld64(f) == want;
         }
         const uint64_t notready = __ballot(!ready && g0 + lane < n_task_tiles);
@@ -1441,7 +1445,7 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     int released_below = 0;  // steps whose slot is known released
     const int pend_last = group_end(a, st->pend_g) - 1;  // last step the task runs
     for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
-      const int step = (a.stage_lo + (int)h) / a.n_tiles;
+      const int step = (a.stage_lo + (int)h) / a.stage_per_step;
       if (step > pend_last) break;
       if (step >= kSlots && step >= released_below) {
         if (ld32(&a.done_count[step - kSlots]) < (uint32_t)a.n_units) break;

@@ -107,6 +107,7 @@ def test_default_opts():
     o = mk.default_opts()
     assert o.split_mode == mk.MK_SPLIT_ADAPTIVE and o.grid_wgs == 0 and o.disable_staging == 0
     assert o.parallel_steps == 0  # automatic: parallel step groups for launches with few units
+    assert o.stage_pieces == 0  # automatic: staging pieces per tile from the problem's size
 
 
 # ---------------------------------------------------------------- host validation
@@ -197,6 +198,8 @@ def test_negative_option_rejected():
     for ps in (-2, 2):
         assert call(q, kv, 4, 1, 1, 4, o, l, mk.default_opts(parallel_steps=ps)) == mk.MK_E_INVAL
         assert b"parallel_steps" in mk.load_library().mk_last_error()
+    assert call(q, kv, 4, 1, 1, 4, o, l, mk.default_opts(stage_pieces=-1)) == mk.MK_E_INVAL
+    assert b"stage_pieces" in mk.load_library().mk_last_error()
 
 
 def test_empty_query_is_a_noop():

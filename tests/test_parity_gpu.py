@@ -244,6 +244,9 @@ def test_bitwise_identical_across_splits_grids_and_delays():
     timing += [dict(stage_delay_ticks=2000), dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
                                                  stage_delay_ticks=5000)]
     timing += [dict(initial_staging_wgs=16, controller_period_us=1), dict(split_mode=mk.MK_SPLIT_ADAPTIVE_PAPER)]
+    # Staging pieces: a tile's 16 KV heads in 1, 3 (6 + 6 + 4), 16 or 5 pieces.
+    timing += [dict(stage_pieces=1), dict(stage_pieces=3), dict(stage_pieces=16, grid_wgs=37),
+               dict(stage_pieces=5, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1, stage_delay_ticks=3000)]
     for v in timing:
         announce(f"variant {v}")
         o, l = run_gpu(qg, kvg, cfg, **v)
@@ -299,6 +302,28 @@ def test_parallel_step_groups_causal_gqa():
     for v in (dict(), dict(steps_per_task=1), dict(steps_per_task=3, grid_wgs=6),
               dict(steps_per_task=4, split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=2, stage_delay_ticks=3000)):
         check_full(cfg, seed=23, parallel_steps=1, **v)
+
+
+def test_staging_pieces_with_ragged_head_ranges():
+    """A tile's five KV heads staged in 1, 2 (3 + 2), 3 (2 + 2 + 1) or 5 pieces, each with
+    its own ready flag that only the units of its heads wait for: every split matches
+    the oracle, the piece count is reported, and the bits do not depend on it."""
+    cfg = shape("pieces_ragged", 6, 4, 320, 320, 10, 5, 64, True)
+    q, kv = make_inputs(cfg, seed=29)
+    qg, kvg = q.cuda(), kv.cuda()
+    ref = None
+    for pieces, want, extra in ((1, 1, {}), (2, 2, dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=1,
+                                                            stage_delay_ticks=3000)),
+                                (3, 3, dict(grid_wgs=4)), (5, 5, {}), (9, 5, dict(parallel_steps=-1)),
+                                (4, 3, dict(split_mode=mk.MK_SPLIT_FIXED, fixed_staging_wgs=3, stage_delay_ticks=2000))):
+        o, l = check_full(cfg, seed=29, stage_pieces=pieces, **extra)
+        st = run_gpu(qg, kvg, cfg, want_stats=True, stage_pieces=pieces, **extra)[2]
+        assert st["stage_pieces"] == want and st["n_stage_tasks"] == st["n_steps"] * st["n_stage_tiles"] * want, st
+        assert st["staging_tasks_done"] == st["n_stage_tasks"], st
+        if extra.get("parallel_steps") is None:
+            if ref is None:
+                ref = (o, l)
+            assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), pieces
 
 
 def test_back_to_back_launches_and_shape_changes():
