@@ -414,56 +414,84 @@ struct Sched {
   int32_t pend_rt, pend_nt;
 };
 
-// Run by lane 0 of wave 0: picks the workgroup's next task and writes (op, x, y).
+// Run by wave 0: picks the workgroup's next task and writes (op, x, y). The control
+// words are shared by every XCD, so each access is a round trip to memory: the wave
+// loads all of them at once, lane-parallel (one round trip), and lane 0 decides from
+// that snapshot, with one more round trip to claim a task (and a rate-limited one for
+// the controller or a role change).
 __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd) {
+  const int lane = threadIdx.x & 63;
+  const Ctrl* cb = a.ctrl;
+  // Lane i < 8: queue head i; then the error word, the staging head, the role count, the
+  // target, the update time, the compute and staging tick sums and task counts. 32-bit
+  // words are read as the low half of a 64-bit load (each sits at the start of its own
+  // 64-byte line).
+  const void* src = lane < kMaxXcd ? (const void*)&cb->xcd_head[lane].v
+                  : lane == 8      ? (const void*)&cb->error.v
+                  : lane == 9      ? (const void*)&cb->stage_head.v
+                  : lane == 10     ? (const void*)&cb->n_stage.v
+                  : lane == 11     ? (const void*)&cb->target.v
+                  : lane == 12     ? (const void*)&cb->ctrl_time.v
+                  : lane == 13     ? (const void*)&cb->compute_ticks.v
+                  : lane == 14     ? (const void*)&cb->compute_done.v
+                  : lane == 15     ? (const void*)&cb->stage_ticks.v
+                                   : (const void*)&cb->stage_done.v;
+  const uint64_t word = lane < 17 ? ld64(reinterpret_cast<const uint64_t*>(src)) : 0ull;
+  auto lane_u32 = [&](int i) { return (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, i); };
+  auto lane_u64 = [&](int i) {
+    return (uint64_t)lane_u32(i) | ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), i) << 32);
+  };
+  uint32_t heads[kMaxXcd];
+#pragma unroll
+  for (int i = 0; i < kMaxXcd; ++i) heads[i] = lane_u32(i);
+  const uint32_t err = lane_u32(8), sh = lane_u32(9), ns = lane_u32(10), tgt_word = lane_u32(11);
+  const uint64_t last = lane_u64(12), c_ticks = lane_u64(13), s_ticks = lane_u64(15);
+  const uint32_t cd = lane_u32(14), sd = lane_u32(16);
+  if (lane != 0) return;
   int32_t op = kOpExit, x = 0, y = 0;
-  if (has_error(a)) {
+  if (err != kErrNone) {
     cmd[0] = kOpExit;
     return;
   }
-  const uint32_t sh = ld32(&a.ctrl->stage_head.v);
   const bool stage_left = (int)sh < a.n_stage_tasks;
+  int tgt = target_of(a, tgt_word);
   // Controller: rate-limited by a compare-and-swap on the update time.
   if (!a.split_fixed) {
-    const uint64_t now = ticks(), last = ld64(&a.ctrl->ctrl_time.v);
+    const uint64_t now = ticks();
     if ((last == 0 || now - last >= a.ctrl_period_ticks) && cas64(&a.ctrl->ctrl_time.v, last, now)) {
       int64_t rp = 0;
       for (int q = 0; q < a.n_xcd; ++q) {
-        const int64_t left = queue_len(a, q) - (int64_t)ld32(&a.ctrl->xcd_head[q].v);
+        const int64_t left = queue_len(a, q) - (int64_t)heads[q];
         rp += left > 0 ? left : 0;
       }
       const int64_t rs = stage_left ? a.n_stage_tasks - (int64_t)sh : 0;
-      const uint64_t cd = ld32(&a.ctrl->compute_done.v), sd = ld32(&a.ctrl->stage_done.v);
       int64_t cp = a.cost_compute0, cs = a.cost_stage0;
       if (a.ctrl_paper) {
         // The paper's inputs: measured busy ticks per finished task.
-        if (cd > 0) cp = (int64_t)(ld64(&a.ctrl->compute_ticks.v) / cd);
-        if (sd > 0) cs = (int64_t)(ld64(&a.ctrl->stage_ticks.v) / sd);
+        if (cd > 0) cp = (int64_t)(c_ticks / cd);
+        if (sd > 0) cs = (int64_t)(s_ticks / sd);
       } else {
         // Measured ticks averaged with the cost model's priors, weighted as one shard's
         // tasks of each role, so the first (cold) tasks do not swing the split.
         const uint64_t kc = (uint64_t)a.n_rtiles * a.n_ntiles, ks = (uint64_t)a.n_chunks * kPieces;
-        cp = (int64_t)((ld64(&a.ctrl->compute_ticks.v) + kc * (uint64_t)a.cost_compute0) / (cd + kc));
-        cs = (int64_t)((ld64(&a.ctrl->stage_ticks.v) + ks * (uint64_t)a.cost_stage0) / (sd + ks));
+        cp = (int64_t)((c_ticks + kc * (uint64_t)a.cost_compute0) / (cd + kc));
+        cs = (int64_t)((s_ticks + ks * (uint64_t)a.cost_stage0) / (sd + ks));
       }
       if (cp < 1) cp = 1;
       if (cs < 1) cs = 1;
-      __hip_atomic_store(&a.ctrl->target.v, (uint32_t)(eq2_target(a.grid, rp, rs, cp, cs) + 1), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      tgt = eq2_target(a.grid, rp, rs, cp, cs);
+      __hip_atomic_store(&a.ctrl->target.v, (uint32_t)(tgt + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       add32(&a.ctrl->ctrl_updates.v, 1);
     }
   }
-  const int tgt = target_of(a, ld32(&a.ctrl->target.v));
   if (!st->pending) {
     // Role changes at task boundaries (§3.2).
     if (st->role == kRoleStage) {
-      const uint32_t ns = ld32(&a.ctrl->n_stage.v);
       if (!stage_left || (!a.split_fixed && (int)ns > tgt && cas32(&a.ctrl->n_stage.v, ns, ns - 1))) {
         if (!stage_left) add32(&a.ctrl->n_stage.v, (uint32_t)-1);
         st->role = kRoleCompute;
       }
     } else if (!a.split_fixed && stage_left) {
-      const uint32_t ns = ld32(&a.ctrl->n_stage.v);
       if ((int)ns < tgt && cas32(&a.ctrl->n_stage.v, ns, ns + 1)) {
         st->role = kRoleStage;
         __hip_atomic_fetch_max(&a.ctrl->max_stage.v, ns + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -480,12 +508,17 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
       add32(&a.ctrl->n_stage.v, (uint32_t)-1);
       st->role = kRoleCompute;
     }
-    // Claim an output tile: this XCD's queue first, then any queue with tiles left.
+    // Claim an output tile: this XCD's queue first, then any queue the snapshot shows
+    // with tiles left.
     const int own = (int)(blockIdx.x % (unsigned)a.n_xcd);
     for (int i = 0; i < a.n_xcd && !st->pending; ++i) {
       const int q = (own + i) % a.n_xcd;
       const int64_t len = queue_len(a, q);
-      if ((int64_t)ld32(&a.ctrl->xcd_head[q].v) >= len) continue;
+      uint32_t hq = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxXcd; ++j)
+        if (j == q) hq = heads[j];
+      if ((int64_t)hq >= len) continue;
       const uint32_t h = add32(&a.ctrl->xcd_head[q].v, 1);
       if ((int64_t)h >= len) continue;
       const int nq = a.xcd_ntiles[q];
@@ -519,7 +552,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
     const int jj = st->pend_rt % a.n_rtiles;
     const int need =
         ((p - 1) * a.n_chunks + min(kChunksPerTile * jj + kChunksPerTile - 1, a.n_chunks - 1)) * kPieces + kPieces - 1;
-    uint32_t h = ld32(&a.ctrl->stage_head.v);
+    uint32_t h = sh;  // a failed compare-and-swap returns the current head
     while ((int)h <= need && (int)h < a.n_stage_tasks) {
       uint32_t expect = h;
       if (__hip_atomic_compare_exchange_strong(&a.ctrl->stage_head.v, &expect, h + 1, __ATOMIC_RELAXED,
@@ -557,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void ag_gemm_kernel(Args a) {
   }
   while (true) {
     __syncthreads();
-    if (tid == 0) schedule(a, &sched, g_cmd);
+    if (tid < 64) schedule(a, &sched, g_cmd);
     __syncthreads();
     const int op = g_cmd[0], x = g_cmd[1], y = g_cmd[2];
     if (op == kOpExit) break;
