@@ -74,8 +74,10 @@ typedef struct {
                                   §3.2 re-targets the staging-workgroup count with
                                   Eq. (2) from measured per-task costs, with two
                                   changes to its inputs: R_p leaves out the compute
-                                  of the last ring step (it can only follow the last
-                                  staging task), and C_p, C_s are averaged with the
+                                  of the last staged ring step (it can only follow the
+                                  last staging task; with parallel step groups staged
+                                  group-interleaved, the last step of every group),
+                                  and C_p, C_s are averaged with the
                                   cost model's priors weighted as one ring step (C_s
                                   counting a staging task's waits for a free slot).
                                   ADAPTIVE_PAPER: Eq. (2) as §3.2 states it, R_p all

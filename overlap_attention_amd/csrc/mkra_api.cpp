@@ -502,6 +502,28 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
   a.grid = grid;
   a.n_xcd = std::min(mkra::kMaxXcd, grid);
   for (int x = 0; x <= a.n_xcd; ++x) a.xcd_unit_begin[x] = (int)((int64_t)x * n_units / a.n_xcd);
+  // Staging order. With parallel step groups every group's first step is needed at
+  // once, so when no slot is reused (n_steps <= kSlots: staging never waits for a free
+  // slot) the steps are staged group-interleaved: every group's first step, then every
+  // group's second, and so on. Otherwise step by step, the order slot reuse needs.
+  a.stage_interleave = a.parallel_steps && a.n_groups > 1 && n_steps <= mkra::kSlots ? 1 : 0;
+  if (a.stage_interleave) {
+    auto rel_first = [&](int g) { return g < a.n_big ? g * a.group : a.n_big * a.group + (g - a.n_big) * a.tail_group; };
+    int pos = 0;
+    for (int r = 0; r < mkra::kMaxGroup; ++r)
+      for (int g = 0; g < a.n_groups; ++g) {
+        const int t = rel_first(g) + r;
+        if (t < std::min(n_steps, rel_first(g + 1))) {
+          a.stage_pos[t] = (int8_t)pos;
+          a.stage_order[pos++] = (int8_t)t;
+        }
+      }
+    if (pos != n_steps) return fail(MK_E_INVAL, "internal: staging order");
+  }
+  // Unit-steps that can only follow the last staging task (ADAPTIVE mode's R_p leaves
+  // them out): the last staged step's, or with an interleaved order the last step of
+  // every group.
+  a.rp_tail = n_units * (int64_t)(a.stage_interleave ? a.n_groups : 1);
   // Running-state slots: one per unit, or one per (unit, step group) with parallel groups.
   const int64_t state_slots = n_units * (a.parallel_steps ? (int64_t)a.n_groups : 1);
 
@@ -530,10 +552,10 @@ mk_status run(const mk_tensor* q, const mk_tensor* kv, int n_chunks, int rank, i
       // Eq. (2) as the paper states it: every compute task remains.
       init = eq2_target_host(grid, n_units * (int64_t)n_steps, n_stage_tasks, a.cost_compute0, a.cost_stage0);
     else
-      // As on the device: R_p without the last ring step, which follows the last
-      // staging task whatever the split.
-      init = eq2_target_host(grid, n_units * (int64_t)(n_steps - 1), n_stage_tasks, a.cost_compute0,
-                             a.cost_stage0);
+      // As on the device: R_p without the unit-steps that follow the last staging task
+      // whatever the split.
+      init = eq2_target_host(grid, std::max<int64_t>(0, n_units * (int64_t)n_steps - a.rp_tail), n_stage_tasks,
+                             a.cost_compute0, a.cost_stage0);
   }
   a.initial_stagers = init;
   a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;

@@ -166,6 +166,11 @@ struct KernelArgs {
   // into slot step % kSlots as blocks of 64 keys per KV head.
   int n_tiles;            // ceil(Lk / 128)
   int n_blocks;           // 2 * n_tiles: blocks per KV head (keys past Lk staged as zeros)
+  int stage_interleave;   // 1: staging position p (of n_steps <= kSlots) stages ring step
+                          // stage_order[p] (parallel step groups: every group's first
+                          // step, then every group's second, ...); 0: position p is step p
+  int8_t stage_order[kSlots];
+  int8_t stage_pos[kSlots];   // its inverse: the staging position of ring step t
   int n_pieces;           // ceil(Hkv / piece_heads)
   int piece_heads;        // KV heads per piece
   int stage_per_step;     // n_tiles * n_pieces: staging tasks (and ready flags) per step
@@ -193,6 +198,8 @@ struct KernelArgs {
   int disable_staging;
   int stage_delay_ticks;
   int debug_flags;        // bit 0: a staging workgroup reads back the K it wrote
+  int64_t rp_tail;        // ADAPTIVE mode: unit-steps R_p leaves out (those that can only
+                          // follow the last staging task)
   int64_t cost_compute0;  // modelled ticks per compute task (controller prior)
   int64_t cost_stage0;    // modelled ticks per staging task (one piece of a tile)
   uint64_t timeout_ticks;

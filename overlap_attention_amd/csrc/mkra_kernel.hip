@@ -121,6 +121,12 @@ __device__ __forceinline__ void raise_error(const KernelArgs& a, uint32_t code) 
   cas32(&a.ctrl->error.v, kErrNone, code);
 }
 
+// Ring step staged at staging position pos (the staging tasks of one position are
+// consecutive).
+__device__ __forceinline__ int stage_step_of(const KernelArgs& a, int pos) {
+  return a.stage_interleave ? (int)a.stage_order[pos & (kSlots - 1)] : pos;
+}
+
 __device__ __forceinline__ int chunk_of_step(const KernelArgs& a, int t) {
   int c = (a.rank - t) % a.n_chunks;
   return c < 0 ? c + a.n_chunks : c;
@@ -235,11 +241,11 @@ __device__ __forceinline__ void maybe_controller(const KernelArgs* ap, const uin
   } else {
     cp = (int64_t)((ct + kc * (uint64_t)a.cost_compute0) / (cd + kc));
     cs = (int64_t)((stt + ks * (uint64_t)a.cost_stage0) / (sd + ks));
-    // R_p counts the compute work that can overlap the remaining staging: every
-    // unit-step of the last ring step needs that step's staged tiles, so it follows the
-    // last staging task whatever the split, and Eq. (2) balances the rest.
-    const int64_t last_step = (int64_t)a.n_units;
-    rp2 = rp > last_step ? rp - last_step : 0;
+    // R_p counts the compute work that can overlap the remaining staging: the
+    // unit-steps of the last staged ring step (with interleaved parallel step groups,
+    // the last step of every group) need tiles staged last, so they follow the last
+    // staging task whatever the split, and Eq. (2) balances the rest.
+    rp2 = rp > a.rp_tail ? rp - a.rp_tail : 0;
   }
   if (cp < 1) cp = 1;
   if (cs < 1) cs = 1;
@@ -422,7 +428,7 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
   static_assert(KCH >= 1 && kBN * CPR % kThreads == 0, "block split");
   const int tid = threadIdx.x, lane = tid & 63;
   const uint64_t t_begin = ticks();
-  const int t = (int)k / a.stage_per_step;
+  const int t = stage_step_of(a, (int)k / a.stage_per_step);
   const int j = ((int)k % a.stage_per_step) / a.n_pieces;
   const int pc = (int)k % a.n_pieces;
   const int g0 = pc * a.piece_heads;               // first KV head of the piece
@@ -452,8 +458,8 @@ __device__ __forceinline__ void stage_tile(const KernelArgs& a, const KernelArgs
           const int q = tid + i * kThreads, r = q / CPR, cc = q % CPR, key = kb * kBN + r;
           const bool in = p < n_pairs && key < a.lk;
           const int64_t off = ((int64_t)key * a.hkv + g) * D + 8 * cc;
-          kr[b][i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + off)) : u32x4{0, 0, 0, 0};
-          vr[b][i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + off)) : u32x4{0, 0, 0, 0};
+          kr[b][i] = in ? *reinterpret_cast<const u32x4*>(kh + off) : u32x4{0, 0, 0, 0};
+          vr[b][i] = in ? *reinterpret_cast<const u32x4*>(vh + off) : u32x4{0, 0, 0, 0};
         }
       }
       uint8_t* scr[NB] = {scratch_buf<0>(), scratch_buf<1>(), scratch_buf<2>(), scratch_buf<3>()};
@@ -1443,10 +1449,19 @@ __device__ __forceinline__ void schedule(const KernelArgs* ap, Sched* st, int32_
     uint32_t h = sh;
     bool assist = false;
     int released_below = 0;  // steps whose slot is known released
-    const int pend_last = group_end(a, st->pend_g) - 1;  // last step the task runs
+    // The last staging position the task needs: its last step's, or with an
+    // interleaved order (no slot is reused, so no staging task waits) the largest
+    // position of its steps; every task up to it may be assisted.
+    int need_pos = group_end(a, st->pend_g) - 1;
+    if (a.stage_interleave) {
+      need_pos = 0;
+      for (int t = group_first(a, st->pend_g); t < group_end(a, st->pend_g); ++t)
+        need_pos = max(need_pos, (int)a.stage_pos[t & (kSlots - 1)]);
+    }
     for (int attempt = 0; attempt < 64 && !a.disable_staging && (int)h < a.n_stage_tasks; ++attempt) {
-      const int step = (a.stage_lo + (int)h) / a.stage_per_step;
-      if (step > pend_last) break;
+      const int pos = (a.stage_lo + (int)h) / a.stage_per_step;
+      if (pos > need_pos) break;
+      const int step = stage_step_of(a, pos);
       if (step >= kSlots && step >= released_below) {
         if (ld32(&a.done_count[step - kSlots]) < (uint32_t)a.n_units) break;
         released_below = step + 1;

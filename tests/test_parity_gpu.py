@@ -447,6 +447,30 @@ def test_stats_and_controller_follow_eq2(mode, groups):
     assert len(seen) == st["n_units"]
 
 
+def test_parallel_groups_stage_interleaved():
+    """Parallel step groups with no slot reused: the staging role takes every group's
+    first step, then every group's second (steps 0, 2, 1, 3 for two groups of two), and
+    ADAPTIVE's R_p leaves out the last step of every group."""
+    cfg = CONFIGS[1]
+    q, kv = make_inputs(cfg, seed=1)
+    announce("traced parallel run")
+    out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2)
+    print("    stats:", st, flush=True)
+    assert st["status"] == 0 and st["parallel_steps"] == 1 and st["step_groups"] == 2 and st["n_steps"] == 4
+    per_step = st["n_stage_tasks"] // st["n_steps"]
+    stage = [r for r in mk.mk_ring_attn_trace() if r[2] == 2]
+    assert len(stage) == st["n_stage_tasks"]
+    for r in stage:
+        task, step = r[3], r[4]
+        assert step == (0, 2, 1, 3)[task // per_step], r
+    ctrl = [r for r in mk.mk_ring_attn_trace() if r[2] == 3]
+    assert ctrl and all(0 <= r[3] <= st["n_units"] * (st["n_steps"] - st["step_groups"]) for r in ctrl)
+    ref = oracle.ring_attention_reference(to_f64(q), to_f64(kv), cfg.rank, cfg.causal, cfg.gqa_ratio)
+    rep = compare(to_f64(out), lse.double().cpu().numpy(), *ref)
+    print("   ", fmt(rep), flush=True)
+    assert rep["ok"], fmt(rep)
+
+
 def test_v_outside_fp16_range_reports_unsupported():
     """The PV product takes V in fp16: a V the fp16 format cannot hold (|v| >= 65536 or
     not finite) in a chunk the call reads ends the launch through the error path and is
