@@ -89,7 +89,11 @@ typedef struct {
                                   index) until staging work runs out, then compute. */
   int32_t fixed_staging_wgs;   /* FIXED mode only: number of staging workgroups. */
   int32_t initial_staging_wgs; /* ADAPTIVE mode: 0 = from the host's cost model of
-                                  Eq. (2) with modelled costs; >0 = start with this. */
+                                  Eq. (2) with modelled costs, or, for a launch whose
+                                  staging fits in one round (at most 8 ring steps and
+                                  at most half of the grid's workgroups in staging
+                                  tasks), one workgroup per staging task; >0 = start
+                                  with this. */
   int32_t grid_wgs;            /* 0 = one workgroup per resident slot (all CUs). */
   int64_t spin_timeout_us;     /* bound of every on-GPU wait; 0 = 10 s. */
   int32_t controller_period_us;/* minimum time between controller updates; 0 = 20 us. */
