@@ -207,8 +207,10 @@ int eq2_target_host(int64_t b, int64_t rp, int64_t rs, int64_t cp, int64_t cs) {
 // task leaves workgroups idle longer at the end of the launch. Measured on MI355X
 // (same-box A/B): steps of Lk*D < 2^19 key-dims (the 32K-token MHA D=64 workload,
 // 1024-token chunks) run best in four-step tasks, 2-9% faster than two-step ones; the
-// 64K-token GQA workload (Lk*D = 2^19) runs best in two-step tasks (0.9% faster than
-// four with a tail), the 128K-token one within 0.5% either way. A tail of shorter tasks
+// 64K-token GQA workload (Lk*D = 2^19) runs best in two-step tasks (0.6-0.9% faster
+// than four with a tail). Above that it depends on the size with no clear rule: four
+// steps with a tail were 0.9% and 1.8% faster at 96K and 128K tokens and 1.5% slower
+// at 192K (same box), so two-step tasks stay the default there. A tail of shorter tasks
 // (the last kDefaultTailSteps steps in tasks of kDefaultTailStepsPerTask) applies only
 // to four-step tasks when the units outnumber the workgroups.
 constexpr int kDefaultTailStepsPerTask = 2;
