@@ -962,8 +962,9 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   auto issue_cur = [&](auto stage_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_tag)::value;
     if (ctile >= ru) {
-      // Wait for this tile's flag, then look at the later flags of the task's tile
-      // sequence 64 at a time (one load per lane) so the next tiles need no check.
+      // Wait for this tile's flag (of the piece holding this unit's KV head), then look
+      // at the later flags of the task's tile sequence 64 at a time (one load per lane)
+      // so the next tiles need no check.
       const int t = t_first + cst;
       ok &= wave_wait_stamp(a, step_flags(a, t, pc) + (cb / kBlocksPerTile) * a.n_pieces, stamp(a.epoch, t), waited);
       int upto = ctile + 1;
