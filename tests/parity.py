@@ -56,15 +56,19 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref):
 def compare_gemm(c_gpu, c_ref, abs_sum, k):
     """GEMM outputs (bf16, fp32 accumulation over K) against the fp64 product.
 
-    Per element the bar is half a bf16 ulp of the exact value (the final rounding) plus
-    the standard bound of an fp32 accumulation, gamma_n * sum_k |a_k w_k| with
-    gamma_n = n * 2^-24 and n = K/16 + 16 (K/16 accumulating MFMA steps, each summing 16
-    products). abs_sum is sum_k |a_k w_k| per element. Returns a report dict;
-    report['ok'] is the verdict, 'worst_over_bar' the largest error / bar ratio."""
+    Per element the bar is the standard bound of an fp32 accumulation, gamma_n * sum_k
+    |a_k w_k| with gamma_n = n * 2^-24 and n = K/16 + 16 (K/16 accumulating MFMA steps,
+    each summing 16 products), plus the final rounding to bf16: half an ulp of the
+    accumulated value, whose magnitude is at most |exact| + that bound (so a sum that
+    crosses into the next binade is held to that binade's ulp). abs_sum is
+    sum_k |a_k w_k| per element. Returns a report dict; report['ok'] is the verdict,
+    'worst_over_bar' the largest error / bar ratio."""
     c_gpu = np.asarray(c_gpu, dtype=np.float64)
     err = np.abs(c_gpu - c_ref)
     n = k / 16 + 16
-    bar = np.where(c_ref != 0, bf16_half_ulp(c_ref), 0.0) + n * 2.0 ** -24 * abs_sum
+    acc = n * 2.0 ** -24 * abs_sum
+    mag = np.abs(c_ref) + acc
+    bar = np.where(mag != 0, bf16_half_ulp(mag), 0.0) + acc
     rep = {"finite": bool(np.isfinite(c_gpu).all()), "max_abs_err": float(err.max()) if err.size else 0.0,
            "worst_over_bar": float((err / np.maximum(bar, 1e-300)).max()) if err.size else 0.0}
     rep["ok"] = rep["finite"] and bool((err <= bar).all())

@@ -50,3 +50,17 @@ def test_gemm_bar_accepts_rounding_and_rejects_a_wrong_term():
     # dropping one k term does not
     wrong = a[:, :-1] @ w[:, :-1].T
     assert not compare_gemm(wrong, ref, abs_sum, 64)["ok"]
+
+
+def test_gemm_bar_at_a_binade_boundary():
+    """An exact value just below 2 whose fp32 sum lands past 2 + 2^-7 rounds to the bf16
+    2 + 2^-6: the error is half an ulp of the upper binade plus the sum's error, which
+    the bar allows; one ulp more is rejected."""
+    from tests.parity import compare_gemm
+
+    k = 64
+    acc = (k / 16 + 16) * 2.0 ** -24
+    abs_sum = np.array([[2 ** -7 / acc * 1.25]])   # accumulation bound 1.25 * 2^-7
+    ref = np.array([[2.0 - 2.0 ** -9]])
+    assert compare_gemm(np.array([[2.0 + 2.0 ** -6]]), ref, abs_sum, k)["ok"]
+    assert not compare_gemm(np.array([[2.0 + 2.0 ** -5]]), ref, abs_sum, k)["ok"]
