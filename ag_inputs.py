@@ -42,6 +42,7 @@ AG_CONFIGS = [
     AgConfig("ag_r3of8_M2048x8_K8192_N4096", n_ranks=8, rank=3, m_loc=2048, k=8192, n_out=4096),
 ]
 AG_CONFIG_BY_NAME = {c.name: c for c in AG_CONFIGS}
+AG_TINY, AG_HEADLINE = AG_CONFIGS
 
 
 def ag_sweep_config(m_total: int, n_ranks: int = 8, k: int = 8192, n_out: int = 4096) -> AgConfig:

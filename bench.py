@@ -334,9 +334,9 @@ def run_ag(args):
     import torch
 
     import overlap_attention_amd as mk
-    from ag_inputs import AG_CONFIG_BY_NAME, AG_CONFIGS, ag_sweep_config, make_ag_inputs
+    from ag_inputs import AG_CONFIG_BY_NAME, AG_HEADLINE, ag_sweep_config, make_ag_inputs
 
-    cfg = AG_CONFIG_BY_NAME[args.ag_workload] if args.ag_workload else AG_CONFIGS[1]
+    cfg = AG_CONFIG_BY_NAME[args.ag_workload] if args.ag_workload else AG_HEADLINE
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -676,7 +676,7 @@ def main():
         return
     if args.ag:
         if args.gpus != 1:
-            print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+            print("bench.py runs on one GPU only: this library has no multi-GPU path (use --gpus 1).", file=sys.stderr)
             sys.exit(2)
         run_ag(args)
         return
@@ -684,21 +684,21 @@ def main():
         print(kernel_stats_from(args.kernel_stats_from, args.warmup, args.steps), flush=True)
         return
     if args.traffic_from:
-        from ring_inputs import CONFIGS, CONFIG_BY_NAME
+        from ring_inputs import CONFIG_BY_NAME, SEQ64K
 
-        cfg = CONFIG_BY_NAME[args.workload] if args.workload else CONFIGS[2]
+        cfg = CONFIG_BY_NAME[args.workload] if args.workload else SEQ64K
         write_traffic(cfg, args.traffic_from, args.copy_calibration_mib or 1024)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     import overlap_attention_amd as mk
-    from ring_inputs import CONFIGS, CONFIG_BY_NAME, make_inputs
+    from ring_inputs import CONFIG_BY_NAME, CONFIGS, SEQ64K, make_inputs
 
-    cfg = CONFIG_BY_NAME[args.workload] if args.workload else CONFIGS[2]
+    cfg = CONFIG_BY_NAME[args.workload] if args.workload else SEQ64K
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     log(f"[bench] workload {cfg.name}: generating inputs")

@@ -44,8 +44,9 @@ class RingConfig:
         return asdict(self)
 
 
-# The five workloads, in order. Index 1 is the small causal MHA case, index 2 the
-# per-rank share of a 64K-token causal GQA sequence over 16 ranks (the headline shape).
+# The five workloads: a tiny D = 64 case, the small causal MHA case, the per-rank share
+# of a 64K-token causal GQA sequence over 16 ranks (the headline shape), the same at 128K
+# tokens with scores doubled, and a 32K-token MHA D = 64 ring.
 CONFIGS = [
     RingConfig("tiny_r0of4_L128_h2_d64_nc", rank=0, n_chunks=4, lq=128, lk=128, hq=2, hkv=2, d=64, causal=False),
     RingConfig("small_r3of8_L1024_h16_d128_causal", rank=3, n_chunks=8, lq=1024, lk=1024, hq=16, hkv=16, d=128,
@@ -59,6 +60,7 @@ CONFIGS = [
 ]
 
 CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+TINY, SMALL, SEQ64K, SEQ128K, SEQ32K_D64 = CONFIGS
 
 
 def make_inputs(cfg: RingConfig, seed: int, device: str = "cpu") -> Tuple[torch.Tensor, torch.Tensor]:

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import overlap_attention_amd as mk
-from ag_inputs import AG_CONFIGS, AgConfig, make_ag_inputs
+from ag_inputs import AG_HEADLINE, AG_TINY, AgConfig, make_ag_inputs
 from tests.parity import compare_gemm, fmt
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ def check(cfg, seed, rows=None, **kw):
 
 
 SHAPES = [
-    AG_CONFIGS[0],
+    AG_TINY,
     AgConfig("ragged_r2of3_M200_K192_N520", n_ranks=3, rank=2, m_loc=200, k=192, n_out=520),
     AgConfig("one_row_r0of5_K64_N8", n_ranks=5, rank=0, m_loc=1, k=64, n_out=8),
     AgConfig("single_rank_M300_K64_N1024", n_ranks=1, rank=0, m_loc=300, k=64, n_out=1024),
@@ -160,7 +160,7 @@ def test_full_size_headline_sampled_rows():
     """The 16K-row, K=8192, N=4096 rank share in the default launch configuration: the
     whole gathered activation bit for bit, and C at the first, last and one random row
     of every 128-row chunk, every column."""
-    cfg = AG_CONFIGS[1]
+    cfg = AG_HEADLINE
     announce(f"{cfg} full size")
     a, w = make_ag_inputs(cfg, 1)
     a_full, c, st = run_gpu(cfg, a.cuda(), w.cuda(), want_stats=True)

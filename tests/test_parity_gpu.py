@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import overlap_attention_amd as mk
-from ring_inputs import CONFIGS, RingConfig, make_inputs, to_f64
+from ring_inputs import SEQ32K_D64, SEQ64K, SEQ128K, SMALL, TINY, RingConfig, make_inputs, to_f64
 from tests.parity import compare, fmt, oracle_rows, wave_slice_rows
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +57,7 @@ def shape(name, n, rank, lq, lk, hq, hkv, d, causal, qk_mult=1.0):
 # --------------------------------------------------------------- the five workloads
 
 def test_tiny_workload_full():
-    check_full(CONFIGS[0], seed=0)
+    check_full(TINY, seed=0)
 
 
 SMALL_SHAPES = [
@@ -81,15 +81,14 @@ def test_small_shapes_full(cfg):
 
 
 def test_small_workload_full():
-    check_full(CONFIGS[1], seed=1)
+    check_full(SMALL, seed=1)
 
 
-def check_full_size(idx, rows, label):
+def check_full_size(cfg, seed, rows, label):
     """A full-size workload in the default launch configuration (as benchmarked),
     compared with the oracle at `rows` (None: every row), all heads."""
-    cfg = CONFIGS[idx]
-    announce(f"{cfg} seed={idx} {label}")
-    q, kv = make_inputs(cfg, seed=idx)
+    announce(f"{cfg} seed={seed} {label}")
+    q, kv = make_inputs(cfg, seed=seed)
     qg, kvg = q.cuda(), kv.cuda()
     out, lse, stats = run_gpu(qg, kvg, cfg, want_stats=True)
     print("    stats:", stats, flush=True)
@@ -110,19 +109,19 @@ def check_full_size(idx, rows, label):
 
 @pytest.mark.timeout(600)
 def test_full_size_64k_every_row():
-    check_full_size(2, None, "every row")
+    check_full_size(SEQ64K, 2, None, "every row")
 
 
 @pytest.mark.timeout(600)
 def test_full_size_128k_every_wave_slice():
-    cfg = CONFIGS[3]
-    check_full_size(3, wave_slice_rows(cfg.lq, per_slice_random=1, seed=3), "first, last and one random row of "
+    cfg = SEQ128K
+    check_full_size(SEQ128K, 3, wave_slice_rows(cfg.lq, per_slice_random=1, seed=3), "first, last and one random row of "
                     "every 32-row slice")
 
 
 @pytest.mark.timeout(600)
 def test_full_size_32k_d64_every_row():
-    check_full_size(4, None, "every row")
+    check_full_size(SEQ32K_D64, 4, None, "every row")
 
 
 SPLIT_VARIANTS = [
@@ -232,7 +231,7 @@ def test_bitwise_identical_across_splits_grids_and_delays():
     timing or the controller. The default mode of this workload runs its step groups in
     parallel (its units fill under half of the device), and that choice is the
     device's, not the grid's."""
-    cfg = CONFIGS[1]
+    cfg = SMALL
     q, kv = make_inputs(cfg, seed=1)
     qg, kvg = q.cuda(), kv.cuda()
     announce("reference split")
@@ -327,7 +326,7 @@ def test_staging_pieces_with_ragged_head_ranges():
 
 
 def test_back_to_back_launches_and_shape_changes():
-    a = CONFIGS[1]
+    a = SMALL
     b = shape("other", 5, 3, 300, 300, 8, 2, 64, True)
     qa, kva = make_inputs(a, seed=21)
     qb, kvb = make_inputs(b, seed=22)
@@ -401,7 +400,7 @@ def test_stats_and_controller_follow_eq2(mode, groups):
     ADAPTIVE_PAPER: R_p is every unclaimed unit-step, and C_p, C_s are plain measured
     averages; the first update's R_p then equals the whole compute work minus what
     was claimed before it."""
-    cfg = CONFIGS[1]
+    cfg = SMALL
     q, kv = make_inputs(cfg, seed=1)
     announce(f"traced {mode} run")
     split = mk.MK_SPLIT_ADAPTIVE if mode == "adaptive" else mk.MK_SPLIT_ADAPTIVE_PAPER
@@ -451,7 +450,7 @@ def test_parallel_groups_stage_interleaved():
     """Parallel step groups with no slot reused: the staging role takes every group's
     first step, then every group's second (steps 0, 2, 1, 3 for two groups of two), and
     ADAPTIVE's R_p leaves out the last step of every group."""
-    cfg = CONFIGS[1]
+    cfg = SMALL
     q, kv = make_inputs(cfg, seed=1)
     announce("traced parallel run")
     out, lse, st = run_gpu(q.cuda(), kv.cuda(), cfg, want_stats=True, trace=1, controller_period_us=2)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import overlap_attention_amd as mk
-from ring_inputs import CONFIGS, RingConfig, make_inputs, to_f64
+from ring_inputs import SEQ64K, SMALL, TINY, RingConfig, make_inputs, to_f64
 from tests.parity import compare, fmt, oracle_rows, wave_slice_rows
 
 pytestmark = pytest.mark.gpu
@@ -40,9 +40,9 @@ def both(cfg, q, kv, copy_wgs):
 
 
 CASES = [
-    (CONFIGS[0], 2),
-    (CONFIGS[1], 16),
-    (CONFIGS[1], 1),
+    (TINY, 2),
+    (SMALL, 16),
+    (SMALL, 1),
     (shape("g4_causal_tail", 3, 2, 320, 320, 8, 2, 128, True, qk_mult=2.0), 4),
     (shape("g8_noncausal_12steps", 12, 5, 384, 384, 8, 1, 128, False), 3),
     (shape("ragged_d64", 5, 4, 200, 200, 6, 3, 64, True), 2),
@@ -63,7 +63,7 @@ def test_unfused_equals_fused_one_step_tasks_and_oracle(cfg, copy_wgs):
 
 @pytest.mark.timeout(600)
 def test_unfused_full_size_64k():
-    cfg = CONFIGS[2]
+    cfg = SEQ64K
     announce(f"{cfg} unfused, full size")
     q, kv = make_inputs(cfg, seed=2)
     (o_u, l_u), (o_f, l_f) = both(cfg, q.cuda(), kv.cuda(), 16)
@@ -77,7 +77,7 @@ def test_unfused_full_size_64k():
 
 
 def test_unfused_then_fused_on_one_workspace():
-    a, b = CONFIGS[1], shape("other", 5, 3, 300, 300, 8, 2, 64, True)
+    a, b = SMALL, shape("other", 5, 3, 300, 300, 8, 2, 64, True)
     qa, kva = make_inputs(a, seed=21)
     qb, kvb = make_inputs(b, seed=22)
     ra = oracle.ring_attention_reference(to_f64(qa), to_f64(kva), a.rank, a.causal, a.gqa_ratio)
@@ -102,7 +102,7 @@ def test_unfused_then_fused_on_one_workspace():
 
 
 def test_unfused_rejects_one_stream():
-    cfg = CONFIGS[0]
+    cfg = TINY
     q, kv = make_inputs(cfg, seed=1)
     q, kv = q.cuda(), kv.cuda()
     o = torch.empty_like(q)
