@@ -4,7 +4,7 @@
                     [--no-cpu-baseline] [--sweep] [--size-sweep] [--unfused] [--verify]
                     [--copy-calibration-mib M]
     python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
-    python bench.py --probes    (MFMA-stream and vector-ALU probes; prints a table)
+    python bench.py --probes    (MFMA-stream, vector-ALU and LDS-read probes; prints a table)
 
 A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
 rank, staging included) over one batch of synthetic input already resident in HBM.
@@ -484,6 +484,8 @@ def run_probes(rounds=3):
     for fn in (lib.mkp_mfma_stream, lib.mkp_valu_rate):
         fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
         fn.restype = ctypes.c_int
+    lib.mkp_lds_rate.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.mkp_lds_rate.restype = ctypes.c_int
 
     def call(fn, mode, iters):
         res = (ctypes.c_double * 4)()
@@ -508,6 +510,17 @@ def run_probes(rounds=3):
         ms, ghz, rate, _ = call(lib.mkp_valu_rate, m, 200000)
         log(f"[probes] {name}: {rate:.1f} lane-ops/clk/CU")
         out.append(f"| {name} | {ms:.1f} | {ghz:.3f} | {rate:.1f} |")
+    out += ["", "| LDS reads (ds_read_b128, no bank conflicts, 8 waves per CU) | ms | shader clock GHz | "
+            "bytes per clock per CU |", "|---|---:|---:|---:|"]
+    lds = []
+    for r in range(rounds):
+        res = (ctypes.c_double * 4)()
+        if lib.mkp_lds_rate(400000, res) != 0:
+            raise RuntimeError("probe failed (LDS rate)")
+        lds.append(list(res))
+        log(f"[probes] round {r} LDS reads: {res[2]:.1f} bytes/clk/CU at {res[1]:.3f} GHz")
+    ms, ghz, rate, _ = sorted(lds, key=lambda x: x[2])[len(lds) // 2]
+    out.append(f"| ds_read_b128 | {ms:.1f} | {ghz:.3f} | {rate:.1f} |")
     return "\n".join(out)
 
 
@@ -656,7 +669,7 @@ def main():
                     help="no GPU: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs (DIR/fetch, DIR/write) into "
                          "profiles/traffic_<workload>.json")
     ap.add_argument("--probes", action="store_true",
-                    help="run the MFMA-stream and vector-ALU probes instead of the benchmark; prints markdown")
+                    help="run the MFMA-stream, vector-ALU and LDS-read probes instead of the benchmark; prints markdown")
     ap.add_argument("--ag", action="store_true",
                     help="benchmark one rank's AllGather+GEMM instead (fused kernel, unfused copy + library GEMM, "
                          "split sweep); prints its own JSON line")

@@ -11,6 +11,9 @@
 //   mkp_valu_rate: vector-ALU issue rate of v_exp_f32 (the transcendental the softmax
 //     needs once per (query, key) pair) and of v_fma_f32, in lane-operations per clock
 //     per CU, to compare against the 4·D MFMA FLOPs that accompany each exp.
+//   mkp_lds_rate: LDS read bandwidth in bytes per clock per CU, 8 waves per CU issuing
+//     ds_read_b128 with no bank conflicts (the compute role reads every MFMA's A
+//     operand from LDS, 1 KiB per product, besides the block copies written into LDS).
 //
 // Each call allocates its buffers, launches one warm-up and one timed grid of one
 // workgroup per CU on the current device, and frees them. Results: ms of the timed
@@ -133,6 +136,33 @@ __global__ __launch_bounds__(kThreads) void valu_rate(float* out, unsigned long 
   out[blockIdx.x * kThreads + tid] = r;
 }
 
+// Every wave reads its own 8 KiB of LDS as eight ds_read_b128 (lanes at consecutive
+// 16-byte addresses, so no bank conflicts), waits for them, and folds one dword of each
+// result into a register so the reads stay live: 8 KiB per wave per iteration.
+__global__ __launch_bounds__(kThreads) void lds_rate(float* out, unsigned long long* clk, int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  static_assert(kLdsBytes == (kThreads / 64) * 8192, "8 KiB of LDS per wave");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kLdsBytes / 4; i += kThreads) reinterpret_cast<uint32_t*>(lds)[i] = mix((uint32_t)i);
+  __syncthreads();
+  const uint32_t base =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)lds) + (uint32_t)w * 8192u + lane * 16u;
+  uint32_t acc = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    u32x4 x0, x1, x2, x3, x4, x5, x6, x7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n ds_read_b128 %1, %8 offset:1024\n ds_read_b128 %2, %8 offset:2048\n"
+        " ds_read_b128 %3, %8 offset:3072\n ds_read_b128 %4, %8 offset:4096\n ds_read_b128 %5, %8 offset:5120\n"
+        " ds_read_b128 %6, %8 offset:6144\n ds_read_b128 %7, %8 offset:7168\n s_waitcnt lgkmcnt(0)"
+        : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7)
+        : "v"(base));
+    acc ^= x0[0] ^ x1[1] ^ x2[2] ^ x3[3] ^ x4[0] ^ x5[1] ^ x6[2] ^ x7[3];
+  }
+  stamp(clk, t0, r0);
+  out[blockIdx.x * kThreads + tid] = (float)acc;
+}
+
 typedef void (*Kern)(float*, unsigned long long*, int);
 
 // One warm-up launch at iters/10, then a timed launch. res = {ms, GHz, cycles per
@@ -209,6 +239,18 @@ extern "C" int mkp_valu_rate(int mode, int iters, double* res) {
   res[0] = r[0];
   res[1] = r[1];
   res[2] = r[2] > 0 ? (double)kThreads * iters * 32 / r[2] : 0.0;
+  res[3] = r[3];
+  return 0;
+}
+
+// iters >= 1 (8 KiB read per wave each). res[4] = {ms, GHz, bytes per clock per CU, CUs}.
+extern "C" int mkp_lds_rate(int iters, double* res) {
+  if (iters < 1 || !res) return 1;
+  double r[4];
+  if (run(lds_rate, iters, r)) return 1;
+  res[0] = r[0];
+  res[1] = r[1];
+  res[2] = r[2] > 0 ? (double)(kThreads / 64) * iters * 8192.0 / r[2] : 0.0;
   res[3] = r[3];
   return 0;
 }
