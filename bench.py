@@ -560,18 +560,24 @@ def oracle_timed(cfg, q, kv, rows, progress=False):
 
 
 def cpu_baseline(cfg, q, kv, budget_rows):
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload:
-    `budget_rows` query rows spread over the chunk, all heads, all keys."""
+    """The fp64 oracle on the host cores, on the same workload: every query row when
+    `budget_rows` is 0 or at least the chunk's rows (the default; about 10 s for the
+    64K-token workload), else `budget_rows` rows spread evenly over the chunk; all
+    heads, all keys."""
     import numpy as np
 
-    rows = np.linspace(0, cfg.lq - 1, budget_rows).astype(np.int64)
+    if budget_rows <= 0 or budget_rows >= cfg.lq:
+        rows, what = None, f"every query row ({cfg.lq})"
+    else:
+        rows = np.linspace(0, cfg.lq - 1, budget_rows).astype(np.int64)
+        what = f"{len(rows)} of {cfg.lq} query rows (evenly spaced)"
     dt, flops, workers = oracle_timed(cfg, q, kv, rows)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(rows)} of {cfg.lq} query rows (evenly spaced), all {cfg.hq} heads, all visible keys; "
+        "sample": f"{what}, all {cfg.hq} heads, all visible keys; "
                   f"{dt:.1f} s on {workers} threads (one KV head per call, BLAS at one thread each; "
                   f"{len(os.sched_getaffinity(0))} cores in the affinity mask) of {_cpu_model()}; fp64 NumPy, "
                   f"dense over masked keys too (FLOPs counted for visible pairs only)",
@@ -652,7 +658,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="name of a workload in ring_inputs.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows of the CPU oracle baseline (0: every row of the workload)")
     ap.add_argument("--repeats", type=int, default=5, help="groups the timed launches are split into (median, min)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time fixed staging splits {1..64} against the adaptive split (Fig. 3's metric)")
@@ -850,7 +857,7 @@ def main():
     if unfused_sweep is not None:
         line["unfused_sweep"] = unfused_sweep
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows or cfg.lq} rows")
         line["cpu_baseline"] = cpu_baseline(cfg, q, kv, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
