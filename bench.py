@@ -4,7 +4,7 @@
                     [--no-cpu-baseline] [--sweep] [--size-sweep] [--unfused] [--verify]
                     [--copy-calibration-mib M]
     python bench.py --traffic-from DIR [--copy-calibration-mib M]   (no GPU)
-    python bench.py --probes    (MFMA-stream, vector-ALU and LDS-read probes; prints a table)
+    python bench.py --probes    (MFMA-stream, vector-ALU, LDS-read and co-execution probes; prints a table)
 
 A step is one call of mk_ring_attn_fwd: the whole hot path (every ring step of one
 rank, staging included) over one batch of synthetic input already resident in HBM.
@@ -486,6 +486,8 @@ def run_probes(rounds=3):
         fn.restype = ctypes.c_int
     lib.mkp_lds_rate.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.mkp_lds_rate.restype = ctypes.c_int
+    lib.mkp_coexec.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.mkp_coexec.restype = ctypes.c_int
 
     def call(fn, mode, iters):
         res = (ctypes.c_double * 4)()
@@ -521,6 +523,19 @@ def run_probes(rounds=3):
         log(f"[probes] round {r} LDS reads: {res[2]:.1f} bytes/clk/CU at {res[1]:.3f} GHz")
     ms, ghz, rate, _ = sorted(lds, key=lambda x: x[2])[len(lds) // 2]
     out.append(f"| ds_read_b128 | {ms:.1f} | {ghz:.3f} | {rate:.1f} |")
+    out += ["", "| two waves per SIMD: first runs MFMAs (32 per iteration, each with a 1 KiB ds_read_b128), "
+            "second one block's softmax per iteration | ms | MFMA wave cycles per iteration | "
+            "softmax wave cycles per iteration |", "|---|---:|---:|---:|"]
+    for mode, name in ((0, "MFMA waves alone"), (1, "softmax waves alone"), (2, "both at once")):
+        runs = []
+        for r in range(rounds):
+            res = (ctypes.c_double * 4)()
+            if lib.mkp_coexec(mode, 20000, res) != 0:
+                raise RuntimeError("probe failed (co-execution mode %d)" % mode)
+            runs.append(list(res))
+            log(f"[probes] round {r} co-execution {name}: MFMA {res[1]:.0f}, softmax {res[2]:.0f} cycles per iteration")
+        ms, cm, cs, _ = sorted(runs, key=lambda x: x[0])[len(runs) // 2]
+        out.append(f"| {name} | {ms:.1f} | {cm:.0f} | {cs:.0f} |")
     return "\n".join(out)
 
 
@@ -676,7 +691,7 @@ def main():
                     help="no GPU: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs (DIR/fetch, DIR/write) into "
                          "profiles/traffic_<workload>.json")
     ap.add_argument("--probes", action="store_true",
-                    help="run the MFMA-stream, vector-ALU and LDS-read probes instead of the benchmark; prints markdown")
+                    help="run the MFMA-stream, vector-ALU, LDS-read and co-execution probes instead of the benchmark; prints markdown")
     ap.add_argument("--ag", action="store_true",
                     help="benchmark one rank's AllGather+GEMM instead (fused kernel, unfused copy + library GEMM, "
                          "split sweep); prints its own JSON line")

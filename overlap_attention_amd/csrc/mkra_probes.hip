@@ -14,6 +14,11 @@
 //   mkp_lds_rate: LDS read bandwidth in bytes per clock per CU, 8 waves per CU issuing
 //     ds_read_b128 with no bank conflicts (the compute role reads every MFMA's A
 //     operand from LDS, 1 KiB per product, besides the block copies written into LDS).
+//   mkp_coexec: the compute role's two-wave pairing on each SIMD, taken apart. The
+//     first wave of a SIMD runs the matrix phase's stream (MFMAs on random bf16, each
+//     fed by a 1 KiB ds_read_b128), the second the softmax phase's instruction mix
+//     (per block: 32 FMAs, 32 exp2, 16 packed fp16 conversions, a 15-add packed fp16
+//     tree), alone or both at once, to see how much each slows the other.
 //
 // Each call allocates its buffers, launches one warm-up and one timed grid of one
 // workgroup per CU on the current device, and frees them. Results: ms of the timed
@@ -163,6 +168,95 @@ __global__ __launch_bounds__(kThreads) void lds_rate(float* out, unsigned long l
   out[blockIdx.x * kThreads + tid] = (float)acc;
 }
 
+// MODE 0: only the MFMA waves run; 1: only the softmax waves; 2: both. The first wave
+// on a SIMD (by HW_ID) takes the MFMA role, the second the softmax role. Lane 0 of
+// each wave writes its role (1 MFMA, 2 softmax, 0 idle) and its s_memtime cycles for
+// `iters` iterations: wave_out[2 * (block * 8 + wave) + {0, 1}].
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void coexec(unsigned long long* wave_out, float* sink, int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ int32_t simd_of[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kLdsBytes / 16; i += kThreads) {
+    u32x4 v;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = mix((uint32_t)(i * 4 + e) * 2654435761u ^ 0x9e3779b9u);
+      v[e] = rand_bf16(x) | (rand_bf16(x >> 16) << 16);
+    }
+    reinterpret_cast<u32x4*>(lds)[i] = v;
+  }
+  if (lane == 0) simd_of[w] = (int32_t)__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));  // HW_ID bits 5:4
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < w; ++v) before += simd_of[v] == simd_of[w];
+  const int role = before == 0 ? 1 : before == 1 ? 2 : 0;
+  const bool run = role != 0 && (MODE == 2 || MODE == role - 1);
+  unsigned long long cyc = 0;
+  float r = 0.f;
+  if (run && role == 1) {
+    // As the compute role issues them: each operand read six MFMAs ahead of its
+    // product, with an explicit wait for the oldest read only.
+    const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)lds) +
+                          (uint32_t)(w & 3) * 16384u + lane * 16u;
+    uint32_t addr[8];
+    for (int k = 0; k < 8; ++k) addr[k] = base + (uint32_t)k * 1024u;
+    bf16x8 b;
+    for (int i = 0; i < 8; ++i) b[i] = (__bf16)((((lane * 37 + i * 11) % 17) - 8) * 0.21f);
+    f32x16 acc[2] = {};
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+      u32x4 buf[6];
+#pragma unroll
+      for (int k = 0; k < 6; ++k) asm volatile("ds_read_b128 %0, %1" : "=v"(buf[k]) : "v"(addr[k]));
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        switch (31 - j < 5 ? 31 - j : 5) {  // reads still in flight after the oldest
+          case 5: asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(buf[j % 6])); break;
+          case 4: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(buf[j % 6])); break;
+          case 3: asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(buf[j % 6])); break;
+          case 2: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(buf[j % 6])); break;
+          case 1: asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(buf[j % 6])); break;
+          default: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(buf[j % 6])); break;
+        }
+        acc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, buf[j % 6]), b, acc[j & 1], 0, 0, 0);
+        if (j + 6 < 32) asm volatile("ds_read_b128 %0, %1" : "=v"(buf[j % 6]) : "v"(addr[(j + 6) & 7]));
+      }
+    }
+    asm volatile("s_nop 0" ::: "memory");
+    for (int i = 0; i < 16; ++i) r += acc[0][i] + acc[1][i];
+    cyc = __builtin_amdgcn_s_memtime() - t0;
+  } else if (run && role == 2) {
+    // One block's softmax per iteration: P = exp2(s c - m) in fp16 pairs, summed by a
+    // tree of packed fp16 adds; m follows the sum, so iterations do not overlap.
+    float s[32];
+    for (int i = 0; i < 32; ++i) s[i] = (((lane * 13 + i * 7) % 23) - 11) * 0.37f;
+    float m = 4.f;
+    const float c = 1.4426950408889634f * 0.125f;
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+      f16x2 p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i][0] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * i], c, -m));
+        p[i][1] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * i + 1], c, -m));
+      }
+#pragma unroll
+      for (int k = 8; k >= 1; k >>= 1)
+#pragma unroll
+        for (int i = 0; i < k; ++i) p[i] = p[i] + p[i + k];
+      m = fmaf((float)p[0][0] + (float)p[0][1], 1e-6f, m);
+    }
+    r = m;
+    cyc = __builtin_amdgcn_s_memtime() - t0;
+  }
+  if (lane == 0) {
+    wave_out[2 * (blockIdx.x * (kThreads / 64) + w)] = (unsigned long long)(run ? role : 0);
+    wave_out[2 * (blockIdx.x * (kThreads / 64) + w) + 1] = cyc;
+  }
+  sink[blockIdx.x * kThreads + tid] = r;
+}
+
 typedef void (*Kern)(float*, unsigned long long*, int);
 
 // One warm-up launch at iters/10, then a timed launch. res = {ms, GHz, cycles per
@@ -253,4 +347,55 @@ extern "C" int mkp_lds_rate(int iters, double* res) {
   res[2] = r[2] > 0 ? (double)(kThreads / 64) * iters * 8192.0 / r[2] : 0.0;
   res[3] = r[3];
   return 0;
+}
+
+// mode 0..2 as for coexec above; iters >= 1 (one iteration: 32 MFMAs for an MFMA wave,
+// one block's softmax for a softmax wave). res[4] = {ms, mean cycles per iteration of
+// the MFMA waves (0 if none ran), the same for the softmax waves, CUs}.
+extern "C" int mkp_coexec(int mode, int iters, double* res) {
+  static void (*const k[3])(unsigned long long*, float*, int) = {coexec<0>, coexec<1>, coexec<2>};
+  if (mode < 0 || mode > 2 || iters < 1 || !res) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 1;
+  const int nw = cus * (kThreads / 64);
+  unsigned long long* wo = nullptr;
+  float* sink = nullptr;
+  unsigned long long* h = new unsigned long long[2 * nw];
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = 0;
+  float ms = 0.f;
+  if (hipMalloc(&wo, sizeof(unsigned long long) * 2 * nw) != hipSuccess ||
+      hipMalloc(&sink, sizeof(float) * kThreads * cus) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+      hipEventCreate(&e1) != hipSuccess) {
+    rc = 1;
+  } else {
+    hipLaunchKernelGGL(k[mode], dim3(cus), dim3(kThreads), 0, nullptr, wo, sink, iters / 10 > 0 ? iters / 10 : 1);
+    rc |= hipDeviceSynchronize() != hipSuccess;
+    rc |= hipEventRecord(e0, nullptr) != hipSuccess;
+    hipLaunchKernelGGL(k[mode], dim3(cus), dim3(kThreads), 0, nullptr, wo, sink, iters);
+    rc |= hipEventRecord(e1, nullptr) != hipSuccess;
+    rc |= hipEventSynchronize(e1) != hipSuccess;
+    rc |= hipGetLastError() != hipSuccess;
+    rc |= hipEventElapsedTime(&ms, e0, e1) != hipSuccess;
+    rc |= hipMemcpy(h, wo, sizeof(unsigned long long) * 2 * nw, hipMemcpyDeviceToHost) != hipSuccess;
+  }
+  if (rc == 0) {
+    double cm = 0, cs = 0;
+    int nm = 0, ns = 0;
+    for (int i = 0; i < nw; ++i) {
+      if (h[2 * i] == 1) { cm += (double)h[2 * i + 1]; ++nm; }
+      if (h[2 * i] == 2) { cs += (double)h[2 * i + 1]; ++ns; }
+    }
+    res[0] = ms;
+    res[1] = nm ? cm / nm / iters : 0.0;
+    res[2] = ns ? cs / ns / iters : 0.0;
+    res[3] = cus;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (wo) (void)hipFree(wo);
+  if (sink) (void)hipFree(sink);
+  delete[] h;
+  return rc;
 }

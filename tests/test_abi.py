@@ -42,19 +42,20 @@ def test_library_exports_every_declared_symbol():
     assert {s for s in exported if not s.startswith("_")} == set(declared_functions())
 
 
-def test_probe_library_exports_its_three_entry_points():
+def test_probe_library_exports_its_four_entry_points():
     # The measurement probes (bench.py --probes) live in a library of their own, so the
     # ring-attention library's ABI stays exactly what include/mkra.h declares.
     path = os.path.join(os.path.dirname(mk.LIB_PATH), "libmkra_probes.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = {s for s in re.findall(r"\bT\s+(\w+)$", out, flags=re.M) if not s.startswith("_")}
-    assert exported == {"mkp_mfma_stream", "mkp_valu_rate", "mkp_lds_rate"}, exported
+    assert exported == {"mkp_mfma_stream", "mkp_valu_rate", "mkp_lds_rate", "mkp_coexec"}, exported
     lib = ctypes.CDLL(path)
     res = (ctypes.c_double * 4)()
     # Bad arguments are refused before any device call.
     assert lib.mkp_mfma_stream(7, 10, res) == 1
     assert lib.mkp_valu_rate(0, 0, res) == 1
     assert lib.mkp_lds_rate(0, res) == 1
+    assert lib.mkp_coexec(3, 10, res) == 1
 
 
 def test_abi_version():
