@@ -56,7 +56,11 @@ typedef struct {
                                   before it on the same stream, which must have had the
                                   same arguments (MK_E_INVAL if no phase-1 call
                                   precedes it). */
-  int32_t reserved[4];
+  int32_t disable_staging;     /* DEBUG (testing the error path): nobody stages and no
+                                  workgroup assists, so the tiles of remote shards wait
+                                  until spin_timeout_us expires and the call reports
+                                  MK_E_TIMEOUT through mk_ag_gemm_status. 0 normally. */
+  int32_t reserved[3];
 } mk_ag_gemm_opts;
 
 /* Filled by mk_allgather_gemm_ex when stats != NULL (the call then synchronises the

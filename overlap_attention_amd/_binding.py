@@ -95,7 +95,8 @@ class mk_ag_gemm_opts(ctypes.Structure):
         ("spin_timeout_us", ctypes.c_int64),
         ("controller_period_us", ctypes.c_int32),
         ("phase", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("disable_staging", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 

@@ -147,6 +147,8 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
       opts.controller_period_us < 0)
     return fail(MK_E_INVAL, "negative option");
   if (opts.phase < 0 || opts.phase > 2) return fail(MK_E_INVAL, "opts.phase must be 0, 1 or 2");
+  if (opts.disable_staging != 0 && (opts.disable_staging != 1 || opts.phase != 0))
+    return fail(MK_E_INVAL, "opts.disable_staging must be 0, or 1 on the fused call (phase 0)");
   if (m_loc == 0) {
     if (stats != nullptr) std::memset(stats, 0, sizeof(*stats));
     return MK_OK;  // nothing to gather or compute
@@ -225,6 +227,8 @@ mk_status run(const mk_tensor* a_shards, int n_ranks, int rank, const mk_tensor*
     init = std::min(opts.initial_staging_wgs, grid - 1 > 0 ? grid - 1 : 0);
   else
     init = eq2_target(grid, n_compute, n_stage, a.cost_compute0, a.cost_stage0);
+  a.disable_staging = opts.disable_staging ? 1 : 0;
+  if (a.disable_staging) init = 0;
   a.initial_stagers = init;
   a.timeout_ticks = (uint64_t)(opts.spin_timeout_us > 0 ? opts.spin_timeout_us : 10000000) * 100ull;
   a.ctrl_period_ticks = (uint64_t)(opts.controller_period_us > 0 ? opts.controller_period_us : 20) * 100ull;

@@ -105,6 +105,7 @@ struct Args {
   int grid;
   int split_fixed;
   int ctrl_paper;
+  int disable_staging;  // error-path testing: no staging role, no assists
   int initial_stagers;
   int64_t cost_compute0, cost_stage0;  // modelled ticks per task
   uint64_t timeout_ticks;

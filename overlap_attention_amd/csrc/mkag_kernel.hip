@@ -453,7 +453,9 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
     cmd[0] = kOpExit;
     return;
   }
-  const bool stage_left = (int)sh < a.n_stage_tasks;
+  // With staging disabled (error-path testing) nothing is staged: no role change, no
+  // drain, no assist.
+  const bool stage_left = !a.disable_staging && (int)sh < a.n_stage_tasks;
   int tgt = target_of(a, tgt_word);
   // Controller: rate-limited by a compare-and-swap on the update time.
   if (!a.split_fixed) {
@@ -548,7 +550,7 @@ __device__ __forceinline__ void schedule(const Args& a, Sched* st, int32_t* cmd)
   // attempts, either with a claim or with the chunks claimed by others (who are
   // staging them: the tile's waits on their flags then end).
   const int p = st->pend_rt / a.n_rtiles;
-  if (p > 0) {
+  if (p > 0 && stage_left) {
     const int jj = st->pend_rt % a.n_rtiles;
     const int need =
         ((p - 1) * a.n_chunks + min(kChunksPerTile * jj + kChunksPerTile - 1, a.n_chunks - 1)) * kPieces + kPieces - 1;

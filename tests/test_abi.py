@@ -75,9 +75,9 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu\n", offsetof(mk_ring_attn_opts, spin_timeout_us), offsetof(mk_ring_attn_opts, trace),
          offsetof(mk_ring_attn_stats, compute_busy_ticks), offsetof(mk_ring_attn_stats, trace_records),
          offsetof(mk_ring_attn_opts, debug_flags), offsetof(mk_ring_attn_stats, debug_mismatches));
-  printf("%zu %zu %zu %zu %zu\n", sizeof(mk_ag_gemm_opts), sizeof(mk_ag_gemm_stats),
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(mk_ag_gemm_opts), sizeof(mk_ag_gemm_stats),
          offsetof(mk_ag_gemm_opts, spin_timeout_us), offsetof(mk_ag_gemm_stats, compute_busy_ticks),
-         offsetof(mk_ag_gemm_stats, wg_ticks));
+         offsetof(mk_ag_gemm_stats, wg_ticks), offsetof(mk_ag_gemm_opts, disable_staging));
   return 0;
 }
 '''
@@ -102,7 +102,8 @@ int main(void) {
     assert [int(x) for x in ag.split()] == [ctypes.sizeof(B.mk_ag_gemm_opts), ctypes.sizeof(B.mk_ag_gemm_stats),
                                             B.mk_ag_gemm_opts.spin_timeout_us.offset,
                                             B.mk_ag_gemm_stats.compute_busy_ticks.offset,
-                                            B.mk_ag_gemm_stats.wg_ticks.offset]
+                                            B.mk_ag_gemm_stats.wg_ticks.offset,
+                                            B.mk_ag_gemm_opts.disable_staging.offset]
 
 
 def test_default_opts():

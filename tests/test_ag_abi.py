@@ -61,6 +61,10 @@ def test_bad_options():
     for ph in (-1, 3):
         assert call(a, 4, 1, w, f, c, mk.ag_default_opts(phase=ph)) == mk.MK_E_INVAL
         assert b"phase" in mk.load_library().mk_last_error()
+    # disable_staging (error-path testing) is 0, or 1 on the fused call only.
+    for kw in (dict(disable_staging=2), dict(disable_staging=-1), dict(disable_staging=1, phase=1)):
+        assert call(a, 4, 1, w, f, c, mk.ag_default_opts(**kw)) == mk.MK_E_INVAL
+        assert b"disable_staging" in mk.load_library().mk_last_error()
 
 
 def test_empty_shards_are_a_noop():
@@ -71,3 +75,4 @@ def test_empty_shards_are_a_noop():
 def test_default_opts():
     o = mk.ag_default_opts()
     assert o.split_mode == mk.MK_SPLIT_ADAPTIVE and o.grid_wgs == 0 and o.spin_timeout_us == 0
+    assert o.disable_staging == 0

@@ -156,6 +156,18 @@ def test_stats_count_every_task():
 
 
 @pytest.mark.timeout(600)
+def test_wait_bound_reports_timeout_and_recovers():
+    cfg = AgConfig("timeout_r1of3_M200_K128_N256", n_ranks=3, rank=1, m_loc=200, k=128, n_out=256)
+    a, w = make_ag_inputs(cfg, 11)
+    announce("staging disabled: the waits for remote shards must expire")
+    mk.allgather_gemm(a.cuda(), cfg.rank, w.cuda(), opts=mk.ag_default_opts(disable_staging=1, spin_timeout_us=100_000))
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_ag_gemm_status()
+    assert e.value.status == mk.MK_E_TIMEOUT
+    announce("next call on the same workspace")
+    check(cfg, seed=11)
+
+
 def test_full_size_headline_sampled_rows():
     """The 16K-row, K=8192, N=4096 rank share in the default launch configuration: the
     whole gathered activation bit for bit, and C at the first, last and one random row
