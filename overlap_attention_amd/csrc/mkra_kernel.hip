@@ -778,6 +778,10 @@ __shared__ uint32_t g_merge;  // parallel step groups: this workgroup's task mer
 template <int D, class ClaimNext>
 __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int step_group, int grp, uint64_t& waited,
                              ClaimNext&& claim_next) {
+  // Where the block copies are issued: at D = 128 from the softmax phase (the matrix
+  // phase, 32 MFMAs, is the longer one there, and each copy instruction holds up the
+  // wave's issue), at D = 64 from the matrix phase (16 MFMAs; the softmax is longer).
+  constexpr bool kCopyInSoftmax = D == 128;
   constexpr int KK = D / 16;                    // k-slices of Q K^T
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int NI = Phase<D>::kChunksPerThread;  // copy instructions per wave per phase
@@ -1067,11 +1071,11 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   // of block m (vector ALU), one s_barrier before each phase. Waves of group 1 take
   // one extra barrier first and group 0 one at the end, so the two waves sharing a
   // SIMD run opposite phases and keep both the matrix cores and the vector ALU busy.
-  // Block m sits in LDS stage m % 4: it is copied during M(m-2), read by QKᵀ in M(m)
-  // and by PV in M(m+1), and its stage is refilled in M(m+2), after a barrier that
-  // both groups pass only once they are done with it. Before every barrier a wave
-  // waits for its own copies of the next block it or the other group reads; the
-  // barrier then makes every wave's part visible.
+  // Block m sits in LDS stage m % 4: it is copied during M(m-2) (at D = 128 during
+  // V(m-2)), read by QKᵀ in M(m) and by PV in M(m+1), and its stage is refilled in
+  // M(m+2) (V(m+2)), after a barrier that both groups pass only once they are done
+  // with it. Before every barrier a wave waits for its own copies of the next block it
+  // or the other group reads; the barrier then makes every wave's part visible.
   // Every wave runs every block of the unit: on the diagonal step the blocks past a
   // wave's last query are fully masked and add exactly zero. The sequence runs
   // straight from the first step's last block into the second step's first.
@@ -1094,19 +1098,26 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
     if constexpr (NP == 8) asm volatile("" : "+v"(pb[4]), "+v"(pb[5]), "+v"(pb[6]), "+v"(pb[7]));
     pin_acc();
   };
-  // Copies: blocks 0 and 1 before the loop, then one block copy threaded through
-  // every M(m), into stage (m+2)%4, which holds block m-2 and is dead by then. The
-  // copy is block m+2 when it exists and its staged tile is known to be ready; else it
-  // copies the discard block (one block after the ring slots, always cache-hot, never
-  // read), and block m+2, if it exists, is copied again after the MFMAs once its flag
-  // is seen (same wave, same LDS addresses, completes later). So every wait below has
-  // at least one block copy issued after the one it needs, and waiting until at most
-  // NI copy instructions are outstanding is enough (it may also cover a discarded
-  // copy).
+  // Copies: blocks 0 and 1 before the loop, then one block copy per block, into stage
+  // (m+2)%4, which holds block m-2 and is dead by then.
+  // - D = 64: threaded through every M(m). The copy is block m+2 when it exists and
+  //   its staged tile is known to be ready; else it copies the discard block (one
+  //   block after the ring slots, always cache-hot, never read), and block m+2, if it
+  //   exists, is copied again after the MFMAs once its flag is seen (same wave, same
+  //   LDS addresses, completes later).
+  // - D = 128: at the start of every V(m), after its barrier: block m+2 (waiting for
+  //   its flag there if its tile is not known ready), or past the end the discard
+  //   block.
+  // Either way every wait below has at least one block copy issued after the one it
+  // needs, so waiting until at most NI copy instructions are outstanding is enough
+  // before a matrix phase (it may also cover a discarded copy). At D = 128 the wait
+  // before a softmax phase drains every copy: the groups run one phase apart, so the
+  // copy a wave issued at the start of its previous softmax phase is read by the other
+  // group's next matrix phase.
   auto wait_block = [&]() __attribute__((always_inline)) { wait_vm(NI); };
-  // M(m): the barrier, the MFMAs, and the copy into stage (S+2)%4. Returns whether the
-  // cursor's block still has to be copied (its tile was not known ready), which the
-  // caller then does with issue_cur before advancing the cursor: kept out of this
+  // M(m): the barrier, the MFMAs, and (D = 64) the copy into stage (S+2)%4. Returns
+  // whether the cursor's block still has to be copied (its tile was not known ready),
+  // which the caller then does with issue_cur before advancing the cursor: kept out of this
   // lambda, because with it inside, the closures nested here kept the compiler from
   // promoting the captured state out of scratch memory.
   auto mstep = [&](int m, auto stage_tag, auto mfmas) __attribute__((always_inline)) {
@@ -1135,11 +1146,20 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   // Operand registers of the next matrix phase's first LDS reads, issued at the end of
   // each softmax phase (MPhase::prefetch).
   u32x4 pre[MPhase<D, 0, true, true>::R];
-  // V(m), then the first operand reads of M(m+1), whose stage is SN.
+  // V(m) (at D = 128 preceded by the copy of block m+2 into stage SN+1), then the
+  // first operand reads of M(m+1), whose stage is SN.
   auto vstep = [&](int m, auto next_stage_tag) __attribute__((always_inline)) {
     constexpr int SN = decltype(next_stage_tag)::value;
-    if (m + 1 < nb) wait_block();
+    if (m + 1 < nb) {
+      if constexpr (kCopyInSoftmax) wait_vm(0);
+      else wait_block();
+    }
     __builtin_amdgcn_s_barrier();
+    if constexpr (kCopyInSoftmax) {
+      if (ck < nb) issue_cur(std::integral_constant<int, (SN + 1) % kStages>{});
+      else dma_block<D, (SN + 1) % kStages>(discard_w, cl, m0w_task);
+      cur_advance();
+    }
     pin_scores();
     softmax();
     sm_advance();
@@ -1147,7 +1167,9 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
     MPhase<D, SN, true, true>::prefetch(pre, la);
   };
 #define MKRA_PVQK(S) \
-  [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) { MPhase<D, S, true, true>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); }
+  [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) {        \
+    MPhase<D, S, true, true, !kCopyInSoftmax>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); \
+  }
 #define MKRA_PV(S) \
   [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) { \
     MPhase<D, S, true, false, false>::run_pre(pre, la, o, pb, s, qr, src, cl, m0w); \
@@ -1167,12 +1189,12 @@ __device__ __forceinline__ void compute_task(const KernelArgs& a, int unit, int 
   // ready, into the stage M(m) left for it, and the cursor's advance.
 #define MKRA_M(m, S, MFMAS)                                                         \
   do {                                                                              \
-    if (mstep(m, std::integral_constant<int, S>{}, MFMAS))                          \
+    if (mstep(m, std::integral_constant<int, S>{}, MFMAS) && !kCopyInSoftmax)       \
       issue_cur(std::integral_constant<int, ((S) + 2) % kStages>{});                \
-    cur_advance();                                                                  \
+    if (!kCopyInSoftmax) cur_advance();                                             \
   } while (0)
   auto first_qk = [&](const uint8_t* src, uint32_t m0w) __attribute__((always_inline)) {
-    MPhase<D, 0, false, true>::run(la, o, pb, s, qr, src, cl, m0w);
+    MPhase<D, 0, false, true, !kCopyInSoftmax>::run(la, o, pb, s, qr, src, cl, m0w);
   };
   MKRA_M(0, 0, first_qk);
   using S0 = std::integral_constant<int, 0>;
