@@ -208,6 +208,12 @@ template <int I>
 __device__ __forceinline__ void copy_one(const uint32_t (&voff)[kCopies], const uint16_t* a_src,
                                          const uint16_t* w_src, uint32_t m0s) {
   const uint32_t m0 = m0s + (uint32_t)(I * kWaves * 1024);
+  // A memory instruction that reads an SGPR a vector instruction wrote needs 5 wait
+  // states first, which the compiler does not keep for inline asm operands. Here the
+  // bases are formed once per tile and advanced by scalar adds, and in the compiled
+  // code no vector write of a base (nor a branch target) lies within 5 wait states of
+  // a copy; the build checks (test_build_isa) hold every build to that, so the copies,
+  // one every other MFMA, carry no s_nop (an s_nop 4 each cost 2 % here).
   if constexpr (I < kCopiesA)
     asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff[I]), "s"(a_src), "{m0}"(m0) : "memory");
   else

@@ -584,19 +584,54 @@ __device__ __forceinline__ void dma_one(const uint8_t* src_w, const CopyLanes<D>
   constexpr int kDst = x < Block<D>::kKBytes ? stage_k<D, S>() + b * Block<D>::kKBytes + x
                                              : stage_v<D, S>() + b * Block<D>::kKBytes + (x - Block<D>::kKBytes);
   const uint32_t m0 = m0w + (uint32_t)kDst;
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(cl.off[I]), "s"(src_w), "{m0}"(m0) : "memory");
+  // A memory instruction that reads an SGPR a vector instruction wrote needs 5 wait
+  // states first. The compiler keeps that distance for its own loads but not for the
+  // SGPR operands of inline asm, and it may set src_w just before with v_readfirstlane
+  // or reload it from a spill with v_readlane; s_nop 4 keeps the distance whatever it
+  // emits.
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(cl.off[I]), "s"(src_w), "{m0}"(m0) : "memory");
 }
 
-template <int D, int S, int... I>
-__device__ __forceinline__ void dma_seq(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w,
-                                        std::integer_sequence<int, I...>) {
-  (dma_one<D, S, I>(src_w, cl, m0w), ...);
+// LDS destination of copy instruction I of a block into stage S, relative to the
+// wave's slice in stage 0 (see dma_one).
+template <int D, int S, int I>
+constexpr int dma_dst() {
+  constexpr int kSrc = I * kThreads * 16;
+  constexpr int b = kSrc / Block<D>::kBytes, x = kSrc % Block<D>::kBytes;
+  return x < Block<D>::kKBytes ? stage_k<D, S>() + b * Block<D>::kKBytes + x
+                               : stage_v<D, S>() + b * Block<D>::kKBytes + (x - Block<D>::kKBytes);
 }
 
-// The whole phase: Phase<D>::kChunksPerThread instructions per wave.
+// The whole phase: Phase<D>::kChunksPerThread instructions per wave, as one asm
+// statement: one s_nop 4 covers the base's last vector write for all of them (nothing
+// can come between), and each m0 write is followed by one wait state before the LDS
+// copy that uses it.
 template <int D, int S>
 __device__ __forceinline__ void dma_block(const uint8_t* src_w, const CopyLanes<D>& cl, uint32_t m0w) {
-  dma_seq<D, S>(src_w, cl, m0w, std::make_integer_sequence<int, Phase<D>::kChunksPerThread>{});
+  constexpr int NI = Phase<D>::kChunksPerThread;
+  static_assert(NI == 2 || NI == 4, "two or four copy instructions per block");
+  if constexpr (NI == 4) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_add_u32 m0, %[m], %[d0]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[src]\n\t"
+        "s_add_u32 m0, %[m], %[d1]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[src]\n\t"
+        "s_add_u32 m0, %[m], %[d2]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o2], %[src]\n\t"
+        "s_add_u32 m0, %[m], %[d3]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o3], %[src]"
+        :
+        : [o0] "v"(cl.off[0]), [o1] "v"(cl.off[1]), [o2] "v"(cl.off[2]), [o3] "v"(cl.off[3]), [src] "s"(src_w),
+          [m] "s"(m0w), [d0] "n"(dma_dst<D, S, 0>()), [d1] "n"(dma_dst<D, S, 1>()), [d2] "n"(dma_dst<D, S, 2>()),
+          [d3] "n"(dma_dst<D, S, 3>())
+        : "memory", "m0", "scc");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_add_u32 m0, %[m], %[d0]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[src]\n\t"
+        "s_add_u32 m0, %[m], %[d1]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[src]"
+        :
+        : [o0] "v"(cl.off[0]), [o1] "v"(cl.off[1]), [src] "s"(src_w), [m] "s"(m0w), [d0] "n"(dma_dst<D, S, 0>()),
+          [d1] "n"(dma_dst<D, S, 1>())
+        : "memory", "m0", "scc");
+  }
 }
 
 // Per-lane LDS addresses of the compute role's operand reads (stage 0, block row 0):
