@@ -26,8 +26,9 @@
 #include "mkra_args.h"
 
 // Operand reads in flight ahead of the MFMA that uses the oldest (matrix phase). With
-// the matrix phase down to MFMAs and operand reads, 2 was fastest (same-box A/B of 2-8:
-// 3.646 ms at 2 against 3.664 at 4 and 3.780 at 6 on the 64K-token workload).
+// the matrix phase down to MFMAs and operand reads, 2 was fastest on the 64K-token
+// workload (same-box A/B runs: 4 was 2.4 % faster than 6, and 2 0.5 % faster than 4;
+// 1 exposes the LDS latency, 22 % slower).
 #ifndef MKRA_LDS_AHEAD
 #define MKRA_LDS_AHEAD 2
 #endif
